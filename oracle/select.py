@@ -1,0 +1,124 @@
+"""Oracle beam selection: per-beam top_k over trie-valid candidates, then top beam_width.
+
+Sources:
+* xLLM generative-recommendation design doc, §4.1.1: every beam expands top_k candidates
+  and the new beam set of size beam_width is chosen from the global beam_width x top_k
+  pool; §4.3: invalid item paths are filtered during the search.
+* FlashRec announcement (SGLang PR thread): with the semantic-ID trie, illegal IDs are
+  never candidates.
+* FlashRec deployment guide, request section: temperature 0 gives a deterministic top-k.
+
+Readings where the pages are silent (each is the plainest one the rest supports):
+* the ranking key of candidate (b, c) is the float32 sum score_b + lp[b, c] (one IEEE
+  rounding); candidates whose key is -inf are not candidates;
+* ties break by key descending, then flat index b * C + c ascending (within one beam this
+  is code ascending); -0.0 and +0.0 compare equal;
+* a beam whose score is -inf is dead and contributes nothing; a beam with fewer than
+  top_k valid children contributes all of them; a pool smaller than beam_width leaves
+  pad slots (token -1, parent -1, score -inf) after all real slots;
+* at level 0 only slot 0 is live (score 0, empty prefix);
+* code c is valid for a beam with prefix p at level l iff p + (c,) is the length-(l+1)
+  prefix of some catalog item (decided from the raw item list).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = np.float32(-np.inf)
+
+
+def catalog_prefix_sets(items: np.ndarray, C: int):
+    """Sorted unique packed prefixes of every length 1..L, from the raw item list.
+
+    Entry l (1-based length) holds the int64 base-C packing of items[:, :l].
+    """
+    items = np.asarray(items, dtype=np.int64)
+    L = items.shape[1]
+    sets = [None]
+    packed = np.zeros(items.shape[0], np.int64)
+    for l in range(1, L + 1):
+        packed = packed * C + items[:, l - 1]
+        sets.append(np.unique(packed))
+    return sets
+
+
+def _is_member(sorted_set: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    idx = np.searchsorted(sorted_set, keys)
+    idx_c = np.minimum(idx, sorted_set.size - 1)
+    return (idx < sorted_set.size) & (sorted_set[idx_c] == keys)
+
+
+def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
+    """One selection step of one request.
+
+    lp        float32 [Wslots][C]   log-probabilities of this step
+    scores    float32 [Wslots]      beam scores (-inf = dead slot)
+    prefixes  list[int | None]      packed prefix of each slot (None for dead slots)
+    level     number of codes already in each live prefix
+    K, W      top_k and beam_width of the request
+    prefix_sets  output of catalog_prefix_sets, or None when unconstrained
+
+    Returns a dict: tokens int32 [W], parents int32 [W], scores float32 [W],
+    prefixes (list of packed prefixes, None for pad slots) and pool_size (the number of
+    candidates that survived the per-beam top_k).
+    """
+    lp = np.asarray(lp, dtype=np.float32)
+    scores = np.asarray(scores, dtype=np.float32)
+    assert not np.isnan(scores).any()
+    all_codes = np.arange(C, dtype=np.int64)
+    pool_key, pool_flat = [], []
+    for b in range(scores.shape[0]):
+        s = scores[b]
+        if s == NEG_INF:
+            continue
+        codes = all_codes
+        if prefix_sets is not None:
+            codes = all_codes[_is_member(prefix_sets[level + 1], prefixes[b] * C + all_codes)]
+        keys = s + lp[b, codes]                       # float32 + float32 -> float32
+        assert keys.dtype == np.float32
+        assert not np.isnan(keys).any(), "NaN log-probability"
+        live = keys != NEG_INF
+        codes, keys = codes[live], keys[live]
+        order = np.lexsort((codes, -keys))[:K]        # full stable sort, keep top_k
+        pool_key.append(keys[order])
+        pool_flat.append(b * C + codes[order])
+    tokens = np.full(W, -1, np.int32)
+    parents = np.full(W, -1, np.int32)
+    out_scores = np.full(W, NEG_INF, np.float32)
+    new_prefixes = [None] * W
+    if pool_key:
+        key = np.concatenate(pool_key)
+        flat = np.concatenate(pool_flat)
+        order = np.lexsort((flat, -key))[:W]
+        n = order.size
+        tokens[:n] = flat[order] % C
+        parents[:n] = flat[order] // C
+        out_scores[:n] = key[order]
+        for i in range(n):
+            new_prefixes[i] = int(prefixes[parents[i]]) * C + int(tokens[i])
+    pool_size = int(sum(k.size for k in pool_key))
+    return dict(tokens=tokens, parents=parents, scores=out_scores, prefixes=new_prefixes,
+                pool_size=pool_size)
+
+
+def initial_beams(W):
+    """Level-0 beam state: slot 0 live with score 0 and the empty prefix."""
+    scores = np.full(W, NEG_INF, np.float32)
+    scores[0] = 0.0
+    prefixes = [None] * W
+    prefixes[0] = 0
+    return scores, prefixes
+
+
+def oracle_beam_search(lp_of_step, W, K, C, S, prefix_sets=None):
+    """S selection steps of one request.  ``lp_of_step(d)`` returns float32 [W][C].
+
+    Returns the list of per-step results of oracle_select.
+    """
+    scores, prefixes = initial_beams(W)
+    steps = []
+    for d in range(S):
+        res = oracle_select(lp_of_step(d), scores, prefixes, d, K, W, C, prefix_sets)
+        steps.append(res)
+        scores, prefixes = res["scores"], res["prefixes"]
+    return steps

@@ -1,0 +1,281 @@
+"""Pins of the oracle beam selection (CPU only).
+
+S1  exhaustive pure-Python enumeration (struct-level float32 keys, counting-based
+    per-beam top_k membership, tuple sort for the global beam_width) on many tiny cases
+    with forced ties, -0.0 and -inf;
+S2  K >= fan-out reduces to the textbook global top-W over all valid (beam, code);
+S3  W = K = 1 is a constrained argmax with the lowest-code tie-break;
+S4  with prefix-keyed log-probabilities and W >= |catalog|, the beam set after L steps is
+    the whole catalog, ordered by the recursively defined tie rule;
+S5  invariants on the synthetic workloads;
+and the candidate-pool size the design doc prints for beam_width = top_k = 512.
+"""
+import os
+import struct
+
+import numpy as np
+import pytest
+
+from oracle.select import catalog_prefix_sets, initial_beams, oracle_beam_search, oracle_select
+from synth import build_trie_csr, catalog_items, logprob_rows, workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NEG_INF = float("-inf")
+
+
+def f32(x: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def enumerate_select(lp, scores, prefixes, level, K, W, C, items):
+    """Independent pure-Python selection by enumeration of the whole W x C grid."""
+    L = len(items[0]) if items else 0
+    prefix_set = {tuple(it[:level + 1]) for it in items} if items is not None else None
+    cands = []
+    for b, s in enumerate(scores):
+        if s == NEG_INF:
+            continue
+        for c in range(C):
+            if prefix_set is not None and tuple(prefixes[b]) + (c,) not in prefix_set:
+                continue
+            key = f32(float(s) + float(lp[b][c]))         # fp32 + fp32, rounded once
+            if key == NEG_INF:
+                continue
+            cands.append((key, b, c))
+    # per-beam top-K membership: fewer than K candidates of the same beam rank above it
+    def better(x, y):   # x ranks strictly above y
+        return x[0] > y[0] or (x[0] == y[0] and x[1] * C + x[2] < y[1] * C + y[2])
+    pool = [x for x in cands if sum(1 for y in cands if y[1] == x[1] and better(y, x)) < K]
+    pool.sort(key=lambda x: (-x[0], x[1] * C + x[2]))
+    sel = pool[:W]
+    tokens = [x[2] for x in sel] + [-1] * (W - len(sel))
+    parents = [x[1] for x in sel] + [-1] * (W - len(sel))
+    sc = [x[0] for x in sel] + [NEG_INF] * (W - len(sel))
+    newp = [tuple(prefixes[x[1]]) + (x[2],) for x in sel] + [None] * (W - len(sel))
+    return tokens, parents, sc, newp, len(pool)
+
+
+def _unpack(p, C, L):
+    out = []
+    for _ in range(L):
+        out.append(p % C)
+        p //= C
+    return tuple(reversed(out))
+
+
+def _run_both(rng, W, K, C, L, n_items, tie_values, steps=None):
+    items = None
+    if n_items:
+        space = C ** L
+        n_items = min(n_items, space)
+        packed = rng.choice(space, size=n_items, replace=False)
+        items = [_unpack(int(p), C, L) for p in packed]
+    psets = catalog_prefix_sets(np.array(items), C) if items is not None else None
+    scores, prefixes = initial_beams(W)
+    tprefixes = [() if p is not None else None for p in prefixes]
+    for level in range(steps or L):
+        if tie_values:
+            lp = rng.choice(np.array([0.0, -0.0, -0.5, -1.0, -np.inf], np.float32), size=(W, C))
+        else:
+            lp = np.minimum(rng.standard_normal((W, C)).astype(np.float32), 0)
+        res = oracle_select(lp, scores, prefixes, level, K, W, C, psets)
+        t2, p2, s2, np2, pool2 = enumerate_select(lp.tolist(), scores.tolist(), tprefixes, level, K, W, C, items)
+        assert res["tokens"].tolist() == t2
+        assert res["parents"].tolist() == p2
+        assert [struct.pack("<f", x) for x in res["scores"].tolist()] == \
+               [struct.pack("<f", x) for x in s2]
+        assert res["pool_size"] == pool2
+        got_prefixes = [None if p is None else _unpack(p, C, level + 1) for p in res["prefixes"]]
+        assert got_prefixes == np2
+        scores, prefixes, tprefixes = res["scores"], res["prefixes"], np2
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_exhaustive_enumeration_tiny_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_cases = int(os.environ.get("GRW_S1_CASES", "2500"))
+    for _ in range(n_cases):
+        W = int(rng.integers(1, 9))
+        K = int(rng.integers(1, 9))
+        C = int(rng.integers(2, 17))
+        L = int(rng.integers(1, 5))
+        n_items = int(rng.integers(0, 41))       # 0 = unconstrained
+        _run_both(rng, W, K, C, L, n_items, tie_values=bool(rng.integers(0, 2)))
+
+
+def test_exhaustive_enumeration_tiny_workload_every_step():
+    """The tiny fp32 workload at full size: every step against enumeration."""
+    wl = workload("tiny")
+    items = catalog_items(wl)
+    psets = catalog_prefix_sets(items, wl.C)
+    steps = oracle_beam_search(lambda d: logprob_rows(wl, d), wl.W, wl.K, wl.C, wl.S, psets)
+    scores, prefixes = initial_beams(wl.W)
+    tpre = [() if p is not None else None for p in prefixes]
+    item_list = [tuple(int(v) for v in it) for it in items]
+    for d, res in enumerate(steps):
+        lp = logprob_rows(wl, d)
+        t, p, s, npre, pool = enumerate_select(lp.tolist(), scores.tolist(), tpre, d, wl.K, wl.W,
+                                               wl.C, item_list)
+        assert res["tokens"].tolist() == t and res["parents"].tolist() == p
+        assert res["scores"].tolist() == s and res["pool_size"] == pool
+        scores, prefixes, tpre = res["scores"], res["prefixes"], npre
+
+
+def test_k_at_least_fanout_is_global_topw():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        W, C, L = int(rng.integers(1, 12)), int(rng.integers(2, 30)), 3
+        items = np.unique(rng.integers(0, C, size=(int(rng.integers(1, 200)), L)), axis=0)
+        psets = catalog_prefix_sets(items, C)
+        K = C                                   # at least every fan-out
+        scores, prefixes = initial_beams(W)
+        for level in range(L):
+            lp = np.minimum(rng.standard_normal((W, C)).astype(np.float32), 0)
+            res = oracle_select(lp, scores, prefixes, level, K, W, C, psets)
+            # textbook: all valid (b, c), lexsort by (-key, flat)
+            keys, flats = [], []
+            for b in range(W):
+                if scores[b] == -np.inf:
+                    continue
+                for c in range(C):
+                    if prefixes[b] * C + c in set(psets[level + 1].tolist()):
+                        keys.append(np.float32(scores[b]) + lp[b, c])
+                        flats.append(b * C + c)
+            keys, flats = np.array(keys, np.float32), np.array(flats)
+            order = np.lexsort((flats, -keys))[:W]
+            n = order.size
+            assert np.array_equal(res["parents"][:n], flats[order] // C)
+            assert np.array_equal(res["tokens"][:n], flats[order] % C)
+            assert np.all(res["parents"][n:] == -1)
+            scores, prefixes = res["scores"], res["prefixes"]
+
+
+def test_width_one_is_constrained_argmax():
+    rng = np.random.default_rng(8)
+    for _ in range(300):
+        C, L = int(rng.integers(2, 20)), 3
+        items = np.unique(rng.integers(0, C, size=(int(rng.integers(1, 60)), L)), axis=0)
+        psets = catalog_prefix_sets(items, C)
+        scores, prefixes = initial_beams(1)
+        path = ()
+        for level in range(L):
+            lp = rng.choice(np.array([0.0, -0.25, -1.0], np.float32), size=(1, C))
+            res = oracle_select(lp, scores, prefixes, level, 1, 1, C, psets)
+            valid = [c for c in range(C) if any(tuple(it[:level + 1]) == path + (c,) for it in items.tolist())]
+            keys = [np.float32(scores[0]) + lp[0, c] for c in valid]
+            best = valid[int(np.argmax(keys))]          # first maximum = lowest code
+            assert res["tokens"][0] == best
+            path = path + (best,)
+            scores, prefixes = res["scores"], res["prefixes"]
+        assert path in {tuple(it) for it in items.tolist()}
+
+
+def test_full_catalog_closed_form():
+    """W >= |catalog|, K >= max fan-out, prefix-keyed log-probs: after L steps the beams are
+    exactly the catalog, ordered by path score with the recursive tie rule."""
+    rng = np.random.default_rng(9)
+    vals = np.array([0.0, -0.5, -1.0, -2.0, -0.125], np.float32)
+    for trial in range(40):
+        C, L = int(rng.integers(2, 7)), int(rng.integers(1, 4))
+        items = np.unique(rng.integers(0, C, size=(int(rng.integers(1, 40)), L)), axis=0)
+        N = len(items)
+        W, K = N + int(rng.integers(0, 3)), C
+        psets = catalog_prefix_sets(items, C)
+        salt = int(rng.integers(0, 2 ** 31))
+
+        def lp_of_prefix(prefix_tuple):
+            h = np.random.default_rng([salt, len(prefix_tuple), *prefix_tuple])
+            return h.choice(vals, size=C)
+
+        # run the oracle, feeding each slot the row keyed by its prefix
+        scores, prefixes = initial_beams(W)
+        tuples = [() if p is not None else None for p in prefixes]
+        for level in range(L):
+            lp = np.zeros((W, C), np.float32)
+            for b in range(W):
+                if tuples[b] is not None:
+                    lp[b] = lp_of_prefix(tuples[b])
+            res = oracle_select(lp, scores, prefixes, level, K, W, C, psets)
+            tuples = [None if p is None else tuples[pa] + (int(t),)
+                      for p, pa, t in zip(res["prefixes"], res["parents"], res["tokens"])]
+            scores, prefixes = res["scores"], res["prefixes"]
+        # closed form: rank every prefix level by level
+        ranked = [((), 0.0)]
+        for level in range(L):
+            nxt = []
+            for slot, (pre, sc) in enumerate(ranked):
+                for c in range(C):
+                    t = pre + (c,)
+                    if any(tuple(it[:level + 1]) == t for it in items.tolist()):
+                        key = f32(sc + float(lp_of_prefix(pre)[c]))
+                        nxt.append((key, slot * C + c, t))
+            nxt.sort(key=lambda x: (-x[0], x[1]))
+            ranked = [(t, k) for k, _, t in nxt]
+        assert [t for t, _ in ranked] == tuples[:N]
+        assert sorted(tuples[:N]) == sorted(tuple(int(v) for v in it) for it in items)
+        assert all(t is None for t in tuples[N:])
+
+
+def _check_invariants(res, lp, scores, prefixes, level, K, W, C, psets):
+    n = int((res["parents"] >= 0).sum())
+    assert np.all(res["parents"][:n] >= 0) and np.all(res["parents"][n:] == -1)
+    assert n == min(W, res["pool_size"])
+    par, tok, sc = res["parents"][:n], res["tokens"][:n], res["scores"][:n]
+    assert np.all(np.isfinite(scores[par]))                       # parents are live
+    recomputed = (scores[par] + lp[par, tok]).astype(np.float32)
+    assert np.array_equal(recomputed.view(np.uint32) & 0x7FFFFFFF, sc.view(np.uint32) & 0x7FFFFFFF)
+    flat = par.astype(np.int64) * C + tok
+    assert np.unique(flat).size == n                              # no duplicates
+    ok = (sc[:-1] > sc[1:]) | ((sc[:-1] == sc[1:]) & (flat[:-1] < flat[1:]))
+    assert np.all(ok)                                             # sorted by the tie rule
+    if psets is not None:
+        newp = np.array([res["prefixes"][i] for i in range(n)], np.int64)
+        assert np.all(np.isin(newp, psets[level + 1]))            # valid catalog prefixes
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen06b"])
+def test_invariants_on_workloads(name):
+    wl = workload(name)
+    items = catalog_items(wl)
+    psets = catalog_prefix_sets(items, wl.C)
+    W = wl.W
+    for r in range(2 if name == "qwen06b" else 1):
+        scores, prefixes = initial_beams(W)
+        for d in range(wl.S):
+            lp = logprob_rows(wl, d)[r * W:(r + 1) * W]
+            res = oracle_select(lp, scores, prefixes, d, wl.K, W, wl.C, psets)
+            _check_invariants(res, lp, scores, prefixes, d, wl.K, W, wl.C, psets)
+            scores, prefixes = res["scores"], res["prefixes"]
+
+
+def test_pool_size_printed_by_design_doc():
+    """tests/golden/pool_size_w512_k512.txt: beam_width = top_k = 512 gives a 262144 pool."""
+    with open(os.path.join(GOLDEN, "pool_size_w512_k512.txt")) as f:
+        fields = dict(line.split("=", 1) for line in f.read().split("\n")
+                      if "=" in line and not line.startswith("#"))
+    W, K, pool = int(fields["beam_width"]), int(fields["top_k"]), int(fields["pool"])
+    C = 1024
+    rng = np.random.default_rng(10)
+    lp = np.minimum(rng.standard_normal((W, C)).astype(np.float32), 0)
+    scores = np.full(W, -1.0, np.float32)          # every slot live
+    res = oracle_select(lp, scores, [0] * W, 1, K, W, C, None)
+    assert res["pool_size"] == pool == W * K
+
+
+def test_csr_trie_agrees_with_catalog_prefixes():
+    """The CSR the GPU consumes encodes exactly the catalog prefix sets (layout check)."""
+    rng = np.random.default_rng(11)
+    C, L = 9, 3
+    items = np.unique(rng.integers(0, C, size=(150, L)), axis=0)
+    t = build_trie_csr(items, C)
+    psets = catalog_prefix_sets(items, C)
+    rp, code = t["row_ptr"], t["code"]
+    # walk every edge: the child's prefix is the parent's prefix extended by the code
+    for n in range(t["n_internal"]):
+        for e in range(rp[n], rp[n + 1]):
+            child = e + 1
+            assert t["node_depth"][child] == t["node_depth"][n] + 1
+            assert t["node_prefix"][child] == t["node_prefix"][n] * C + code[e]
+        assert np.all(np.diff(code[rp[n]:rp[n + 1]]) > 0)
+    for l in range(1, L + 1):
+        assert np.array_equal(np.sort(t["node_prefix"][t["node_depth"] == l]), psets[l])
