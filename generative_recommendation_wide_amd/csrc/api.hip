@@ -1,0 +1,435 @@
+// C-ABI layer: workspace, argument validation, batch binding and kernel dispatch.
+//
+// Everything the decode step needs on the device is allocated once in grw_ws_create
+// (xLLM generative-recommendation design doc, section 3.2: prepare the space, indices and
+// structures of later steps up front; section 4.3: reuse candidate containers instead of
+// creating them every round).  grw_ws_bind_batch uploads per-request descriptors and the
+// shared-stage work list once per batch; the per-step calls only enqueue kernels.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "grw_internal.h"
+
+using namespace grw;
+
+struct grw_ws {
+  grw_limits lim;
+  int device = 0;
+  int n_cu = 256;
+  bool mfma = false;            // shared stage on the bf16 MFMA kernel
+  // device buffers
+  ReqDesc* d_req = nullptr;
+  int32_t* d_slot_req = nullptr;
+  ShWork* d_work = nullptr;
+  int64_t work_cap = 0;
+  float* d_opart = nullptr;
+  float* d_lpart = nullptr;
+  float* d_ou = nullptr;
+  float* d_lu = nullptr;
+  uint64_t* d_pool = nullptr;
+  int64_t pool_cap = 0;
+  uint32_t* d_pool_count = nullptr;
+  uint32_t* d_bound = nullptr;
+  int32_t* d_flags = nullptr;
+  // pinned host staging for the bind upload
+  void* h_stage = nullptr;
+  size_t stage_bytes = 0;
+  // bound batch (host mirror)
+  bool bound = false;
+  int R = 0;
+  int sumW = 0;
+  int maxW = 0, maxK = 0;
+  int n_work = 0;
+  std::vector<ReqDesc> req;
+};
+
+namespace {
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GRW_OK : GRW_EDEVICE; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dtype_ok(int t) { return t == GRW_F32 || t == GRW_BF16 || t == GRW_FP8_E4M3; }
+
+int64_t mfma_items_bound(const grw_limits& L, int g) {
+  const int64_t mt = ceil_div((int64_t)L.max_total_beams * g, kShRows) + L.max_requests;
+  return (int64_t)L.Hkv * mt * L.max_splits;
+}
+
+template <typename T>
+int dev_alloc(T** p, int64_t n) {
+  if (n <= 0) n = 1;
+  if (hipMalloc((void**)p, (size_t)n * sizeof(T)) != hipSuccess) {
+    *p = nullptr;
+    return GRW_ENOMEM;
+  }
+  return GRW_OK;
+}
+
+void free_all(grw_ws* w) {
+  (void)hipFree(w->d_req);
+  (void)hipFree(w->d_slot_req);
+  (void)hipFree(w->d_work);
+  (void)hipFree(w->d_opart);
+  (void)hipFree(w->d_lpart);
+  (void)hipFree(w->d_ou);
+  (void)hipFree(w->d_lu);
+  (void)hipFree(w->d_pool);
+  (void)hipFree(w->d_pool_count);
+  (void)hipFree(w->d_bound);
+  (void)hipFree(w->d_flags);
+  if (w->h_stage) (void)hipHostFree(w->h_stage);
+}
+
+// Shared-stage work list of the MFMA kernel.  Items of one (request, kv head, split)
+// share the same prompt tiles; they are assigned to one XCD (workgroup i runs on XCD
+// i % 8) so the repeated tile reads are served by that XCD's L2.
+void build_mfma_work(grw_ws* w, std::vector<ShWork>& out) {
+  const grw_limits& L = w->lim;
+  const int g = L.Hq / L.Hkv;
+  // balance: aim for >= 2 workgroups per CU, splitting long prompts
+  int64_t total_tiles = 0;
+  for (const ReqDesc& r : w->req)
+    total_tiles += (int64_t)L.Hkv * ceil_div((int64_t)r.W * g, kShRows) * ceil_div(r.P, kShKeys);
+  const int64_t target_items = 2LL * w->n_cu;
+  const int64_t tiles_per_item = std::max<int64_t>(4, ceil_div(total_tiles, target_items));
+  struct Group { int r, h, split, p0, p1, n_items; int64_t tiles; };
+  std::vector<Group> groups;
+  for (int ri = 0; ri < w->R; ++ri) {
+    ReqDesc& r = w->req[ri];
+    const int64_t ptiles = ceil_div(r.P, kShKeys);
+    int ns = (int)std::min<int64_t>(L.max_splits, std::max<int64_t>(1, ceil_div(ptiles, tiles_per_item)));
+    const int64_t chunk_tiles = ceil_div(ptiles, ns);
+    ns = (int)ceil_div(ptiles, chunk_tiles);
+    r.nsplit = ns;
+    const int mt = (int)ceil_div((int64_t)r.W * g, kShRows);
+    for (int s = 0; s < ns; ++s) {
+      const int p0 = (int)(s * chunk_tiles * kShKeys);
+      const int p1 = (int)std::min<int64_t>(r.P, (s + 1) * chunk_tiles * kShKeys);
+      for (int h = 0; h < L.Hkv; ++h)
+        groups.push_back({ri, h, s, p0, p1, mt, (int64_t)mt * ceil_div(p1 - p0, kShKeys)});
+    }
+  }
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group& a, const Group& b) { return a.tiles > b.tiles; });
+  constexpr int NX = 8;
+  std::vector<std::vector<ShWork>> q(NX);
+  std::vector<int64_t> load(NX, 0);
+  for (const Group& gr : groups) {
+    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += gr.tiles;
+    for (int m = 0; m < gr.n_items; ++m)
+      q[x].push_back({gr.r, gr.h, m * kShRows, gr.split, gr.p0, gr.p1, 0, 0});
+  }
+  size_t len = 0;
+  for (auto& v : q) len = std::max(len, v.size());
+  out.clear();
+  for (size_t j = 0; j < len; ++j)
+    for (int x = 0; x < NX; ++x)
+      out.push_back(j < q[x].size() ? q[x][j] : ShWork{-1, 0, 0, 0, 0, 0, 0, 0});
+}
+
+// Work list of the generic VALU shared stage: one item per (slot, query head, split).
+void build_valu_work(grw_ws* w, std::vector<ShWork>& out) {
+  const grw_limits& L = w->lim;
+  out.clear();
+  for (int ri = 0; ri < w->R; ++ri) {
+    ReqDesc& r = w->req[ri];
+    const int ns = (int)ceil_div(r.P, kValuMaxKeys);
+    r.nsplit = ns;
+    for (int b = 0; b < r.W; ++b)
+      for (int qh = 0; qh < L.Hq; ++qh)
+        for (int s = 0; s < ns; ++s) {
+          const int p0 = s * kValuMaxKeys;
+          const int p1 = std::min(r.P, (s + 1) * kValuMaxKeys);
+          out.push_back({ri, qh, b, s, p0, p1, 0, 0});
+        }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* grw_status_str(int s) {
+  switch (s) {
+    case GRW_OK: return "ok";
+    case GRW_EINVAL: return "invalid argument";
+    case GRW_ENOMEM: return "out of memory";
+    case GRW_EDEVICE: return "HIP runtime error";
+    case GRW_EUNSUPPORTED: return "unsupported shape or dtype";
+    case GRW_ESTATE: return "invalid call order (bind a batch first)";
+    default: return "unknown status";
+  }
+}
+
+int grw_ws_create(const grw_limits* limits, grw_ws** out) {
+  if (!limits || !out) return GRW_EINVAL;
+  *out = nullptr;
+  grw_limits L = *limits;
+  if (L.max_splits == 0) L.max_splits = 8;
+  if (L.max_requests < 1 || L.max_total_beams < 1 || L.max_W < 1 || L.max_K < 1 || L.max_C < 1 ||
+      L.max_S < 1 || L.max_P < 1 || L.Hq < 1 || L.Hkv < 1 || L.D < 4 || L.max_splits < 1)
+    return GRW_EINVAL;
+  if (!dtype_ok(L.q_dtype) || !dtype_ok(L.kv_dtype) || L.q_dtype == GRW_FP8_E4M3) return GRW_EINVAL;
+  if (L.max_W > kMaxW || L.max_K > kMaxK || L.max_S > 64 || L.max_splits > 16) return GRW_EUNSUPPORTED;
+  if (L.max_W > L.max_total_beams) return GRW_EINVAL;
+  if (L.Hq % L.Hkv != 0) return GRW_EINVAL;
+  const int g = L.Hq / L.Hkv;
+  if (g != 1 && g != 2 && g != 4) return GRW_EUNSUPPORTED;
+  const int hd = L.Hkv * L.D;
+  if (hd != 128 && hd != 256 && hd != 512 && hd != 1024) return GRW_EUNSUPPORTED;
+  if (L.D % 4 != 0 || L.D > 256) return GRW_EUNSUPPORTED;
+  if ((uint64_t)L.max_W * (uint64_t)L.max_C >= (1ull << 32)) return GRW_EUNSUPPORTED;
+
+  grw_ws* w = new (std::nothrow) grw_ws();
+  if (!w) return GRW_ENOMEM;
+  w->lim = L;
+  if (hipGetDevice(&w->device) != hipSuccess) { delete w; return GRW_EDEVICE; }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, w->device) == hipSuccess && cu > 0)
+    w->n_cu = cu;
+  w->mfma = L.D == 128 && L.q_dtype == GRW_BF16 &&
+            (L.kv_dtype == GRW_BF16 || L.kv_dtype == GRW_FP8_E4M3);
+  if (!w->mfma && (int64_t)L.max_P > (int64_t)L.max_splits * kValuMaxKeys) {
+    delete w;
+    return GRW_EUNSUPPORTED;
+  }
+  const int64_t B = L.max_total_beams;
+  const int64_t items = w->mfma ? 2 * mfma_items_bound(L, g) + 8 * 256 + 64
+                                : B * L.Hq * L.max_splits;
+  w->work_cap = items;
+  w->pool_cap = B * (int64_t)L.max_K;
+  int st = GRW_OK;
+  if (st == GRW_OK) st = dev_alloc(&w->d_req, L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_slot_req, B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_work, items);
+  if (st == GRW_OK) st = dev_alloc(&w->d_opart, (int64_t)L.max_splits * B * L.Hq * L.D);
+  if (st == GRW_OK) st = dev_alloc(&w->d_lpart, (int64_t)L.max_splits * B * L.Hq);
+  if (st == GRW_OK) st = dev_alloc(&w->d_ou, B * L.Hq * L.D);
+  if (st == GRW_OK) st = dev_alloc(&w->d_lu, B * L.Hq);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pool, w->pool_cap);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pool_count, L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
+  if (st == GRW_OK) {
+    w->stage_bytes = sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * B + sizeof(ShWork) * items;
+    if (hipHostMalloc(&w->h_stage, w->stage_bytes, hipHostMallocDefault) != hipSuccess) {
+      w->h_stage = nullptr;
+      st = GRW_ENOMEM;
+    }
+  }
+  if (st == GRW_OK) {
+    if (hipMemset(w->d_pool_count, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
+        hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
+        hipMemset(w->d_flags, 0, sizeof(int32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess)
+      st = GRW_EDEVICE;
+  }
+  if (st != GRW_OK) {
+    free_all(w);
+    delete w;
+    return st;
+  }
+  *out = w;
+  return GRW_OK;
+}
+
+int grw_ws_destroy(grw_ws* w) {
+  if (!w) return GRW_EINVAL;
+  (void)hipDeviceSynchronize();
+  free_all(w);
+  delete w;
+  return GRW_OK;
+}
+
+int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32_t* K_host,
+                      const int32_t* P_host, void* stream) {
+  if (!w || !W_host || !K_host || !P_host) return GRW_EINVAL;
+  const grw_limits& L = w->lim;
+  if (n_requests < 1 || n_requests > L.max_requests) return GRW_EINVAL;
+  std::vector<ReqDesc> req(n_requests);
+  int64_t sumW = 0, kv = 0, pool = 0;
+  int maxW = 0, maxK = 0;
+  for (int r = 0; r < n_requests; ++r) {
+    const int W = W_host[r], K = K_host[r], P = P_host[r];
+    if (W < 1 || W > L.max_W || K < 1 || K > L.max_K || P < 1 || P > L.max_P) return GRW_EINVAL;
+    ReqDesc& d = req[r];
+    d.boff = (int32_t)sumW;
+    d.W = W; d.K = K; d.P = P;
+    d.Pp = (int32_t)ceil_div(P, kPadP) * kPadP;
+    d.nsplit = 1;
+    d.kv_off = kv * L.Hkv * L.D;
+    d.pool_off = pool;
+    sumW += W;
+    kv += d.Pp;
+    pool += (int64_t)W * K;
+    maxW = std::max(maxW, W);
+    maxK = std::max(maxK, K);
+  }
+  if (sumW > L.max_total_beams || pool > w->pool_cap) return GRW_EINVAL;
+  if (!w->mfma) {
+    for (const ReqDesc& d : req)
+      if (ceil_div(d.P, kValuMaxKeys) > L.max_splits) return GRW_EUNSUPPORTED;
+  }
+  w->req = req;
+  w->R = n_requests;
+  w->sumW = (int)sumW;
+  std::vector<ShWork> work;
+  if (w->mfma) build_mfma_work(w, work);
+  else build_valu_work(w, work);
+  if ((int64_t)work.size() > w->work_cap) return GRW_EUNSUPPORTED;
+  // one upload: descriptors, slot -> request map, work list
+  uint8_t* h = (uint8_t*)w->h_stage;
+  ReqDesc* hreq = (ReqDesc*)h;
+  int32_t* hslot = (int32_t*)(h + sizeof(ReqDesc) * L.max_requests);
+  ShWork* hwork = (ShWork*)(h + sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * L.max_total_beams);
+  std::memcpy(hreq, w->req.data(), sizeof(ReqDesc) * n_requests);
+  for (int r = 0; r < n_requests; ++r)
+    for (int b = 0; b < req[r].W; ++b) hslot[req[r].boff + b] = r;
+  std::memcpy(hwork, work.data(), sizeof(ShWork) * work.size());
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(w->d_req, hreq, sizeof(ReqDesc) * n_requests, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(w->d_slot_req, hslot, sizeof(int32_t) * sumW, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !work.empty())
+    e = hipMemcpyAsync(w->d_work, hwork, sizeof(ShWork) * work.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    w->bound = false;
+    return GRW_EDEVICE;
+  }
+  w->n_work = (int)work.size();
+  w->maxW = maxW;
+  w->maxK = maxK;
+  w->bound = true;
+  return GRW_OK;
+}
+
+int grw_beams_init(grw_ws* w, float* beam_scores, int32_t* beam_node, void* stream) {
+  if (!w || !beam_scores || !beam_node) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  return hip_status(launch_beams_init(w->d_req, w->d_slot_req, w->sumW, beam_scores, beam_node,
+                                      (hipStream_t)stream));
+}
+
+int beam_attn_decode(grw_ws* w, const void* q, const void* k_shared, const void* v_shared,
+                     const float* k_scale, const float* v_scale, const void* k_unshared,
+                     const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                     float* out, void* stream) {
+  if (!w) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  const grw_limits& L = w->lim;
+  if (!q || !k_shared || !v_shared || !k_unshared || !v_unshared || !parent_idx || !out)
+    return GRW_EINVAL;
+  const bool fp8 = L.kv_dtype == GRW_FP8_E4M3;
+  if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return GRW_EINVAL;
+  if (step < 0 || step >= L.max_S) return GRW_EINVAL;
+  AttnArgs a{};
+  a.req = w->d_req;
+  a.slot_req = w->d_slot_req;
+  a.q = q;
+  a.k_shared = k_shared;
+  a.v_shared = v_shared;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_unshared = k_unshared;
+  a.v_unshared = v_unshared;
+  a.parent_idx = parent_idx;
+  a.step = step;
+  a.out = out;
+  a.opart = w->d_opart;
+  a.lpart = w->d_lpart;
+  a.ou = w->d_ou;
+  a.lu = w->d_lu;
+  a.flags = w->d_flags;
+  a.sumW = w->sumW;
+  a.Hq = L.Hq;
+  a.Hkv = L.Hkv;
+  a.D = L.D;
+  a.g = L.Hq / L.Hkv;
+  a.q_dtype = L.q_dtype;
+  a.kv_dtype = L.kv_dtype;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = w->mfma ? launch_attn_shared_mfma(a, w->d_work, w->n_work, s)
+                         : launch_attn_shared_valu(a, w->d_work, w->n_work, s);
+  if (e == hipSuccess) e = launch_attn_unshared(a, s);
+  if (e == hipSuccess) e = launch_attn_merge(a, s);
+  return hip_status(e);
+}
+
+int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, const int32_t* beam_node,
+                const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
+                int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
+                float* out_score, int32_t* out_node, void* stream) {
+  if (!w) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  const grw_limits& L = w->lim;
+  if (!logprobs || !beam_scores || !out_token || !out_parent || !out_score || !out_node)
+    return GRW_EINVAL;
+  const bool trie = trie_row_ptr != nullptr || trie_code != nullptr;
+  if (trie && (!trie_row_ptr || !trie_code || !beam_node || trie_n_internal < 1)) return GRW_EINVAL;
+  if (W != w->maxW || K != w->maxK) return GRW_EINVAL;
+  if (C < 1 || C > L.max_C) return GRW_EINVAL;
+  if ((uint64_t)w->maxW * (uint64_t)C >= (1ull << 32)) return GRW_EUNSUPPORTED;
+  if ((const void*)out_score == (const void*)beam_scores || (const void*)out_node == (const void*)beam_node)
+    return GRW_EINVAL;
+  SelArgs a{};
+  a.req = w->d_req;
+  a.slot_req = w->d_slot_req;
+  a.logprobs = logprobs;
+  a.scores = beam_scores;
+  a.nodes = beam_node;
+  a.row_ptr = trie ? trie_row_ptr : nullptr;
+  a.code = trie ? trie_code : nullptr;
+  a.n_internal = trie_n_internal;
+  a.C = C;
+  a.sumW = w->sumW;
+  a.R = w->R;
+  a.pool = w->d_pool;
+  a.pool_count = w->d_pool_count;
+  a.bound = w->d_bound;
+  a.out_token = out_token;
+  a.out_parent = out_parent;
+  a.out_score = out_score;
+  a.out_node = out_node;
+  a.flags = w->d_flags;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_select_topk(a, s);
+  if (e == hipSuccess) e = launch_select_global(a, s);
+  return hip_status(e);
+}
+
+int grw_backtrack(grw_ws* w, const int32_t* tokens, const int32_t* parents, int32_t S,
+                  int32_t* sid_out, void* stream) {
+  if (!w || !tokens || !parents || !sid_out) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  if (S < 1 || S > w->lim.max_S) return GRW_EINVAL;
+  return hip_status(launch_backtrack(w->d_req, w->d_slot_req, w->sumW, tokens, parents, S, sid_out,
+                                     (hipStream_t)stream));
+}
+
+int grw_ws_error(grw_ws* w, void* stream, int32_t* flags) {
+  if (!w || !flags) return GRW_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t v = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&v, w->d_flags, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(w->d_flags, 0, sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  *flags = v;
+  return hip_status(e);
+}
+
+int grw_ws_splits(const grw_ws* w, int32_t r, int32_t* n_splits) {
+  if (!w || !n_splits) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  if (r < 0 || r >= w->R) return GRW_EINVAL;
+  *n_splits = w->req[r].nsplit;
+  return GRW_OK;
+}
+
+}  // extern "C"

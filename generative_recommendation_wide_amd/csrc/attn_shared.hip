@@ -1,0 +1,341 @@
+// Shared stage of beam attention (xLLM generative-recommendation design doc, section 4.2.2,
+// stage 1): every beam's queries attend to the request's prompt KV only, producing a
+// normalised partial output and its log-sum-exp.  The prompt KV is stored once per
+// request (section 4.2.1) and each tile of it is streamed from HBM into LDS once per
+// workgroup, where it is reused by 128 query rows (64 beams x 2 heads for grouped heads
+// of 2); workgroups of one (request, kv head) are placed on one XCD so their repeated
+// tile reads hit that XCD's L2 rather than HBM.
+//
+// MFMA path (D = 128, bf16 queries, bf16 or fp8 KV): per wave 32 query rows,
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys x queries), so each lane owns one
+//   query column and the row max / sum need only one cross-lane step;
+//   O^T += V^T P^T with the same instruction, P kept in registers (the key order inside a
+//   16-key step is permuted identically in V^T and P^T, which leaves the sum unchanged).
+// fp8 codes are widened to bf16 exactly while being written to LDS; the key scale joins
+// the softmax scale and the value scale multiplies the output.
+#include "device_common.h"
+#include "grw_internal.h"
+
+namespace grw {
+
+namespace {
+
+constexpr int DH = 128;
+constexpr int NT = kShKeys;            // 64 keys per tile
+constexpr int KS = DH + 8;             // LDS row stride (bf16) of the K tile: 272 B
+constexpr int VS = NT + 4;             // LDS row stride (bf16) of the V^T tile: 136 B
+constexpr int K_TILE = NT * KS;        // bf16 elements
+constexpr int V_TILE = DH * VS;
+
+template <bool FP8>
+struct TileRegs {
+  // bf16: K 4 x 16 B, V^T 4 x 16 B per thread; fp8: 2 + 2 x 16 B
+  static constexpr int N = FP8 ? 2 : 4;
+  u32x4 k[N];
+  u32x4 v[N];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void load_tile(TileRegs<FP8>& t, const uint8_t* kb, const uint8_t* vb,
+                                          int p, int Pp, int tid) {
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 4, dc = c & 15;   // 16 chunks of 8 bf16 per key row
+      t.k[i] = *(const u32x4*)(kb + ((size_t)(p + key) * DH + dc * 8) * 2);
+      const int d = c >> 3, kc = c & 7;      // 8 chunks of 8 keys per V^T row
+      t.v[i] = *(const u32x4*)(vb + ((size_t)d * Pp + p + kc * 8) * 2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 3, dc = c & 7;    // 8 chunks of 16 codes per key row
+      t.k[i] = *(const u32x4*)(kb + (size_t)(p + key) * DH + dc * 16);
+      const int d = c >> 2, kc = c & 3;      // 4 chunks of 16 codes per V^T row
+      t.v[i] = *(const u32x4*)(vb + (size_t)d * Pp + p + kc * 16);
+    }
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void store_tile(const TileRegs<FP8>& t, __bf16* sk, __bf16* sv, int tid) {
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 4, dc = c & 15;
+      *(u32x4*)(sk + key * KS + dc * 8) = t.k[i];
+      const int d = c >> 3, kc = c & 7;
+      u32x2* dst = (u32x2*)(sv + d * VS + kc * 8);   // rows are 8-byte aligned
+      dst[0] = u32x2{t.v[i].x, t.v[i].y};
+      dst[1] = u32x2{t.v[i].z, t.v[i].w};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int key = c >> 3, dc = c & 7;
+      u32x2 a = fp8x4_to_bf16x4(t.k[i].x), b = fp8x4_to_bf16x4(t.k[i].y);
+      u32x2 e = fp8x4_to_bf16x4(t.k[i].z), f = fp8x4_to_bf16x4(t.k[i].w);
+      u32x4* kd = (u32x4*)(sk + key * KS + dc * 16);
+      kd[0] = u32x4{a.x, a.y, b.x, b.y};
+      kd[1] = u32x4{e.x, e.y, f.x, f.y};
+      const int d = c >> 2, kc = c & 3;
+      u32x2* vd = (u32x2*)(sv + d * VS + kc * 16);
+      vd[0] = fp8x4_to_bf16x4(t.v[i].x);
+      vd[1] = fp8x4_to_bf16x4(t.v[i].y);
+      vd[2] = fp8x4_to_bf16x4(t.v[i].z);
+      vd[3] = fp8x4_to_bf16x4(t.v[i].w);
+    }
+  }
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, const ShWork* __restrict__ work) {
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_TILE + V_TILE)];
+  const ShWork wk = work[blockIdx.x];
+  if (wk.r < 0) return;
+  const ReqDesc rd = a.req[wk.r];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = a.g, Hq = a.Hq, h = wk.h;
+  const int nrows = rd.W * g;
+
+  // this lane's query row (the B-operand column of S^T and of O^T)
+  const int mrow = wk.m0 + wave * 32 + l32;
+  const bool row_ok = mrow < nrows;
+  const int b = row_ok ? mrow / g : 0;
+  const int qh = h * g + (row_ok ? mrow - b * g : 0);
+  const int slot = rd.boff + b;
+
+  bf16x8 qf[DH / 16];
+  {
+    const __bf16* qrow = (const __bf16*)a.q + ((size_t)slot * Hq + qh) * DH;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      if (row_ok) {
+        qf[ks] = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  const size_t esz = FP8 ? 1 : 2;
+  const uint8_t* kb = (const uint8_t*)a.k_shared + (rd.kv_off + (size_t)h * rd.Pp * DH) * esz;
+  const uint8_t* vb = (const uint8_t*)a.v_shared + (rd.kv_off + (size_t)h * DH * rd.Pp) * esz;
+
+  float c = rsqrtf((float)DH) * kLog2e;     // softmax scale in log2 units
+  float vscale = 1.0f;
+  if constexpr (FP8) {
+    c *= a.k_scale[h];
+    vscale = a.v_scale[h];
+  }
+
+  const int p0 = wk.p0, p1 = wk.p1;
+  const int ntiles = (p1 - p0 + NT - 1) / NT;
+
+  // LDS: K tiles [2][NT][KS], then V^T tiles [2][DH][VS]
+  __bf16* const sk0 = smem;
+  __bf16* const sv0 = smem + 2 * K_TILE;
+
+  TileRegs<FP8> regs;
+  load_tile<FP8>(regs, kb, vb, p0, rd.Pp, tid);
+  store_tile<FP8>(regs, sk0, sv0, tid);
+  __syncthreads();
+
+  float m_run = -INFINITY;   // running max of scaled scores (identical on both lane halves)
+  float l_run = 0.0f;        // this lane's share of the running sum
+  floatx16 o[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) o[db] = floatx16{};
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int p = p0 + t * NT;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile<FP8>(regs, kb, vb, p + NT, rd.Pp, tid);
+
+    // S^T (64 keys x 32 queries) in two 32-key blocks
+    floatx16 s0 = floatx16{}, s1 = floatx16{};
+    const __bf16* kt = sk0 + buf * K_TILE;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      const bf16x8 a0 = *(const bf16x8*)(kt + l32 * KS + ks * 16 + hi * 8);
+      const bf16x8 a1 = *(const bf16x8*)(kt + (32 + l32) * KS + ks * 16 + hi * 8);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+    }
+    // value k of block kb belongs to key p + kb*32 + (k/4)*8 + hi*4 + k%4
+    if (p + NT > p1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int key = p + (k >> 2) * 8 + hi * 4 + (k & 3);
+        if (key >= p1) s0[k] = -INFINITY;
+        if (key + 32 >= p1) s1[k] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s0[k], s1[k]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);   // m_run = -inf -> 0
+    float psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      s0[k] = fast_exp2(fmaf(s0[k], c, -m_new));
+      s1[k] = fast_exp2(fmaf(s1[k], c, -m_new));
+      psum += s0[k] + s1[k];
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db) o[db] *= alpha;
+
+    // P^T fragments: k-step ks covers 16 keys; lane half `hi` supplies its 8 values
+    bf16x8 pb[4];
+    pb[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+    pb[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+    pb[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+    pb[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+
+    const __bf16* vt = sv0 + buf * V_TILE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kb0 = (ks >> 1) * 32 + (ks & 1) * 16 + hi * 4;   // first key of the lane's run
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        const __bf16* row = vt + (db * 32 + l32) * VS;
+        const bf16x4 v0 = *(const bf16x4*)(row + kb0);
+        const bf16x4 v1 = *(const bf16x4*)(row + kb0 + 8);
+        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[db], 0, 0, 0);
+      }
+    }
+
+    if (more) store_tile<FP8>(regs, sk0 + (buf ^ 1) * K_TILE, sv0 + (buf ^ 1) * V_TILE, tid);
+    __syncthreads();
+  }
+
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = vscale / l;
+  float* dst = a.opart + (((size_t)wk.split * a.sumW + slot) * Hq + qh) * DH;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
+                   o[db][i * 4 + 3] * inv};
+      *(floatx4*)(dst + db * 32 + i * 8 + hi * 4) = v;
+    }
+  }
+  if (hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------------
+// Generic VALU shared stage: one workgroup per (slot, query head, split), any dtype and
+// head dim <= 256.  Used for float32 inputs and shapes the MFMA kernel does not cover.
+// Work item fields: r, h = query head, m0 = request-local slot, split, p0, p1.
+// ---------------------------------------------------------------------------------------
+template <int KVT>
+__device__ __forceinline__ float kv_load(const void* base, size_t i) {
+  if constexpr (KVT == GRW_F32) return ((const float*)base)[i];
+  else if constexpr (KVT == GRW_BF16) return bf16_bits_to_f32(((const uint16_t*)base)[i]);
+  else {
+    const uint32_t byte = ((const uint8_t*)base)[i];
+    return fp8x2_to_f32<false>(byte).x;
+  }
+}
+
+template <int KVT>
+__global__ __launch_bounds__(256) void attn_shared_valu_kernel(AttnArgs a, const ShWork* __restrict__ work) {
+  __shared__ float qs[256];
+  __shared__ float ss[kValuMaxKeys];
+  __shared__ float red[8];
+  const ShWork wk = work[blockIdx.x];
+  if (wk.r < 0) return;
+  const ReqDesc rd = a.req[wk.r];
+  const int tid = threadIdx.x, D = a.D, qh = wk.h, hk = qh / a.g;
+  const int slot = rd.boff + wk.m0;
+  const size_t qi = ((size_t)slot * a.Hq + qh) * D;
+  for (int d = tid; d < D; d += 256)
+    qs[d] = a.q_dtype == GRW_F32 ? ((const float*)a.q)[qi + d]
+                                 : bf16_bits_to_f32(((const uint16_t*)a.q)[qi + d]);
+  __syncthreads();
+  float c = rsqrtf((float)D) * kLog2e;
+  float vscale = 1.0f;
+  if (KVT == GRW_FP8_E4M3) {
+    c *= a.k_scale[hk];
+    vscale = a.v_scale[hk];
+  }
+  const size_t kbase = rd.kv_off + (size_t)hk * rd.Pp * D;   // [Pp][D]
+  const size_t vbase = rd.kv_off + (size_t)hk * D * rd.Pp;   // [D][Pp]
+  const int n = wk.p1 - wk.p0;
+  float mx = -INFINITY;
+  for (int t = tid; t < n; t += 256) {
+    const size_t row = kbase + (size_t)(wk.p0 + t) * D;
+    float s = 0.0f;
+    for (int d = 0; d < D; ++d) s = fmaf(qs[d], kv_load<KVT>(a.k_shared, row + d), s);
+    s *= c;
+    ss[t] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.0f;
+  for (int t = tid; t < n; t += 256) {
+    const float p = fast_exp2(ss[t] - mx);
+    ss[t] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = sum;
+  __syncthreads();
+  sum = red[4] + red[5] + red[6] + red[7];
+  for (int d = tid; d < D; d += 256) {
+    const size_t vrow = vbase + (size_t)d * rd.Pp + wk.p0;
+    float acc = 0.0f;
+    for (int t = 0; t < n; ++t) acc = fmaf(ss[t], kv_load<KVT>(a.v_shared, vrow + t), acc);
+    a.opart[(((size_t)wk.split * a.sumW + slot) * a.Hq + qh) * D + d] = acc * vscale / sum;
+  }
+  if (tid == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * a.Hq + qh] = (mx + fast_log2(sum)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_attn_shared_mfma(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  if (a.kv_dtype == GRW_FP8_E4M3)
+    attn_shared_mfma_kernel<true><<<n_work, 256, 0, s>>>(a, work);
+  else
+    attn_shared_mfma_kernel<false><<<n_work, 256, 0, s>>>(a, work);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_shared_valu(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  switch (a.kv_dtype) {
+    case GRW_F32: attn_shared_valu_kernel<GRW_F32><<<n_work, 256, 0, s>>>(a, work); break;
+    case GRW_BF16: attn_shared_valu_kernel<GRW_BF16><<<n_work, 256, 0, s>>>(a, work); break;
+    default: attn_shared_valu_kernel<GRW_FP8_E4M3><<<n_work, 256, 0, s>>>(a, work); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace grw

@@ -1,0 +1,224 @@
+// Unshared stage and merge of beam attention (xLLM generative-recommendation design doc,
+// section 4.2.2 stages 2 and 3; section 4.2.1 for the token-granular decode KV).
+//
+// Unshared stage: one wavefront per beam slot.  The wave walks the beam's parent
+// pointers (j_d = b, j_{e-1} = parent[e][j_e]) and attends to the d + 1 decode tokens of
+// its ancestry directly where they were written — no block copy, no reorder of the decode
+// KV after selection.  Each lane holds E = Hkv*D/64 contiguous elements of the token's
+// K and V rows (one kv head spans D/E lanes) and the matching elements of the beam's G
+// query heads of that kv head; the next parent pointer is loaded together with the
+// current token's K/V so the pointer chase overlaps the KV reads.
+//
+// Merge: per (slot, query head) the partials i (the shared stage's splits and the
+// unshared stage) combine as lse = log sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i
+// (online-softmax merge).  Dead slots (negative parent pointer at this depth) get zeros.
+#include "device_common.h"
+#include "grw_internal.h"
+
+namespace grw {
+
+namespace {
+
+template <int KVT, int E>
+__device__ __forceinline__ void load_row(const void* base, size_t off, float (&x)[E]) {
+  if constexpr (KVT == GRW_F32) {
+    const float* p = (const float*)base + off;
+#pragma unroll
+    for (int i = 0; i < E; i += 2) {
+      floatx2 v = *(const floatx2*)(p + i);
+      x[i] = v.x;
+      x[i + 1] = v.y;
+    }
+  } else if constexpr (KVT == GRW_BF16) {
+    const uint16_t* p = (const uint16_t*)base + off;
+    if constexpr (E >= 8) {
+#pragma unroll
+      for (int i = 0; i < E; i += 8) {
+        u32x4 w = *(const u32x4*)(p + i);
+        x[i + 0] = __uint_as_float(w.x << 16); x[i + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+        x[i + 2] = __uint_as_float(w.y << 16); x[i + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+        x[i + 4] = __uint_as_float(w.z << 16); x[i + 5] = __uint_as_float(w.z & 0xFFFF0000u);
+        x[i + 6] = __uint_as_float(w.w << 16); x[i + 7] = __uint_as_float(w.w & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; i += 2) {
+        uint32_t w = *(const uint32_t*)(p + i);
+        x[i] = __uint_as_float(w << 16);
+        x[i + 1] = __uint_as_float(w & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const uint8_t* p = (const uint8_t*)base + off;
+    if constexpr (E >= 4) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4) {
+        const uint32_t w = *(const uint32_t*)(p + i);
+        floatx2 lo = fp8x2_to_f32<false>(w), hi = fp8x2_to_f32<true>(w);
+        x[i] = lo.x; x[i + 1] = lo.y; x[i + 2] = hi.x; x[i + 3] = hi.y;
+      }
+    } else {
+      const uint32_t w = *(const uint16_t*)p;
+      floatx2 lo = fp8x2_to_f32<false>(w);
+      x[0] = lo.x; x[1] = lo.y;
+    }
+  }
+}
+
+template <int KVT, int E, int G>
+__global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= a.sumW) return;
+  const int sumW = a.sumW, D = a.D, Hq = a.Hq;
+  const int LPH = D / E;                 // lanes per kv head
+  const int hk = lane / LPH;             // this lane's kv head
+  const int d0 = (lane - hk * LPH) * E;  // first head-dim element of this lane
+  const int step = a.step;
+
+  const int par = a.parent_idx[(size_t)step * sumW + slot];
+  if (par < 0) return;                   // dead slot: the merge writes zeros
+  const ReqDesc rd = a.req[a.slot_req[slot]];
+  const int Wr = rd.W, boff = rd.boff;
+
+  float q[G][E];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const size_t qi = ((size_t)slot * Hq + hk * G + j) * D + d0;
+    if (a.q_dtype == GRW_F32) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) q[j][i] = ((const float*)a.q)[qi + i];
+    } else {
+      load_row<GRW_BF16, E>(a.q, qi, q[j]);
+    }
+  }
+  float c = rsqrtf((float)D) * kLog2e;
+  float vscale = 1.0f;
+  if constexpr (KVT == GRW_FP8_E4M3) {
+    c *= a.k_scale[hk];
+    vscale = a.v_scale[hk];
+  }
+
+  float m[G], l[G], o[G][E];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[j][i] = 0.0f;
+  }
+
+  const size_t tok = (size_t)a.Hkv * D;        // elements per decode token row
+  int j = slot - boff;                          // request-local slot at depth e
+  bool bad = false;
+  for (int e = step; e >= 0; --e) {
+    const size_t off = ((size_t)e * sumW + boff + j) * tok + (size_t)hk * D + d0;
+    float kx[E], vx[E];
+    load_row<KVT, E>(a.k_unshared, off, kx);
+    load_row<KVT, E>(a.v_unshared, off, vx);
+    int nj = 0;
+    if (e > 0) nj = a.parent_idx[(size_t)e * sumW + boff + j];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) s = fmaf(q[jj][i], kx[i], s);
+      for (int w = 1; w < LPH; w <<= 1) s += __shfl_xor(s, w, 64);
+      s *= c;
+      const float mn = fmaxf(m[jj], s);
+      const float alpha = fast_exp2(m[jj] - mn);
+      const float p = fast_exp2(s - mn);
+      l[jj] = fmaf(l[jj], alpha, p);
+#pragma unroll
+      for (int i = 0; i < E; ++i) o[jj][i] = fmaf(o[jj][i], alpha, p * vx[i]);
+      m[jj] = mn;
+    }
+    if (e > 0) {
+      if (nj < 0 || nj >= Wr) { bad = true; break; }
+      j = nj;
+    }
+  }
+  if (bad) {
+    if (lane == 0) atomicOr(a.flags, (int)GRW_FLAG_BAD_PARENT);
+    return;
+  }
+#pragma unroll
+  for (int jj = 0; jj < G; ++jj) {
+    const float inv = vscale / l[jj];
+    float* dst = a.ou + ((size_t)slot * Hq + hk * G + jj) * D + d0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) dst[i] = o[jj][i] * inv;
+    if (lane == hk * LPH) a.lu[(size_t)slot * Hq + hk * G + jj] = (m[jj] + fast_log2(l[jj])) * kLn2;
+  }
+}
+
+// one thread per (slot, query head, 4 head-dim elements)
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  const int D4 = a.D >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.sumW * a.Hq * D4;
+  if (idx >= total) return;
+  const int slot = (int)(idx / ((int64_t)a.Hq * D4));
+  const int rem = (int)(idx - (int64_t)slot * a.Hq * D4);
+  const int qh = rem / D4, d4 = rem - qh * D4;
+  floatx4* dst = (floatx4*)(a.out + ((size_t)slot * a.Hq + qh) * a.D) + d4;
+  if (a.parent_idx[(size_t)a.step * a.sumW + slot] < 0) {
+    *dst = floatx4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const int ns = a.req[a.slot_req[slot]].nsplit;
+  const size_t row = (size_t)slot * a.Hq + qh;
+  const size_t plane = (size_t)a.sumW * a.Hq;
+  const float lu = a.lu[row];
+  float M = lu;
+  for (int i = 0; i < ns; ++i) M = fmaxf(M, a.lpart[i * plane + row]);
+  float wsum = fast_exp2((lu - M) * kLog2e);
+  floatx4 acc = ((const floatx4*)(a.ou + row * a.D))[d4] * wsum;
+  for (int i = 0; i < ns; ++i) {
+    const float w = fast_exp2((a.lpart[i * plane + row] - M) * kLog2e);
+    acc += ((const floatx4*)(a.opart + (i * plane + row) * a.D))[d4] * w;
+    wsum += w;
+  }
+  *dst = acc * (1.0f / wsum);
+}
+
+template <int KVT, int E>
+hipError_t launch_unshared_g(const AttnArgs& a, hipStream_t s, int blocks) {
+  switch (a.g) {
+    case 1: attn_unshared_kernel<KVT, E, 1><<<blocks, 256, 0, s>>>(a); break;
+    case 2: attn_unshared_kernel<KVT, E, 2><<<blocks, 256, 0, s>>>(a); break;
+    default: attn_unshared_kernel<KVT, E, 4><<<blocks, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int KVT>
+hipError_t launch_unshared_e(const AttnArgs& a, hipStream_t s, int blocks) {
+  switch ((a.Hkv * a.D) / 64) {
+    case 2: return launch_unshared_g<KVT, 2>(a, s, blocks);
+    case 4: return launch_unshared_g<KVT, 4>(a, s, blocks);
+    case 8: return launch_unshared_g<KVT, 8>(a, s, blocks);
+    default: return launch_unshared_g<KVT, 16>(a, s, blocks);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s) {
+  const int blocks = (a.sumW + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  switch (a.kv_dtype) {
+    case GRW_F32: return launch_unshared_e<GRW_F32>(a, s, blocks);
+    case GRW_BF16: return launch_unshared_e<GRW_BF16>(a, s, blocks);
+    default: return launch_unshared_e<GRW_FP8_E4M3>(a, s, blocks);
+  }
+}
+
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.sumW * a.Hq * (a.D / 4);
+  if (total == 0) return hipSuccess;
+  attn_merge_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace grw

@@ -1,0 +1,63 @@
+"""Device-resident multi-step decode loop (xLLM generative-recommendation design doc,
+section 3.2: fixed-step execution prepares every step's buffers up front and keeps the
+rounds on the device with no per-step device-to-host round trip; section 6: each round
+runs the forward, the beam search and the next round's input preparation on the device).
+
+Per step d: beam_select picks the new beams (their parents become row d of parent_idx),
+then beam_attn_decode runs once per layer at depth d.  Beam state ping-pongs between two
+preallocated buffers; nothing in run() synchronises with the host.  grw_backtrack turns
+(token, parent) rows into the final semantic-ID tuples.
+"""
+from __future__ import annotations
+
+import torch
+
+
+class DecodeLoop:
+    def __init__(self, ws, S: int, C: int, trie=None, device="cuda"):
+        """ws: a bound Workspace; trie: (row_ptr, code, n_internal) device tensors or None."""
+        from . import _lib  # noqa: F401  (the library must be loaded)
+        self.ws, self.S, self.C = ws, S, C
+        sumW = ws.sumW
+        self.W = max(ws.W)
+        self.K = max(ws.K)
+        self.trie = trie
+        dev = torch.device(device)
+        self.scores = torch.empty(2, sumW, dtype=torch.float32, device=dev)
+        self.nodes = torch.empty(2, sumW, dtype=torch.int32, device=dev)
+        self.tokens = torch.empty(S, sumW, dtype=torch.int32, device=dev)
+        self.parents = torch.empty(S, sumW, dtype=torch.int32, device=dev)   # parent_idx
+        self.sid = torch.empty(sumW, S, dtype=torch.int32, device=dev)
+
+    def select_step(self, d: int, logprobs, stream=None):
+        from . import beam_select
+        cur, nxt = d % 2, (d + 1) % 2
+        row_ptr, code, n_int = self.trie if self.trie is not None else (None, None, 0)
+        beam_select(self.ws, logprobs, self.scores[cur], self.nodes[cur], row_ptr, code, n_int,
+                    self.W, self.K, self.C, self.tokens[d], self.parents[d], self.scores[nxt],
+                    self.nodes[nxt], stream)
+
+    def attn_step(self, d: int, layer, out, stream=None):
+        from . import beam_attn_decode
+        beam_attn_decode(self.ws, layer["q"][d], layer["k_s"], layer["v_s"], layer.get("k_scale"),
+                         layer.get("v_scale"), layer["k_u"], layer["v_u"], self.parents, d, out, stream)
+
+    def run(self, logprobs, layers, out, stream=None, steps=None):
+        """logprobs: sequence of S device tensors [sumW][C]; layers: sequence of dicts with
+        q [S][sumW][Hq][D], k_s, v_s, k_scale, v_scale, k_u, v_u (device tensors);
+        out: [sumW][Hq][D] float32 device tensor, or a list with one per layer."""
+        from . import grw_backtrack
+        steps = self.S if steps is None else steps
+        self.ws.beams_init(self.scores[0], self.nodes[0], stream)
+        for d in range(steps):
+            self.select_step(d, logprobs[d], stream)
+            for li, layer in enumerate(layers):
+                self.attn_step(d, layer, out[li] if isinstance(out, (list, tuple)) else out, stream)
+        if steps == self.S:
+            grw_backtrack(self.ws, self.tokens, self.parents, self.S, self.sid, stream)
+
+    def final_scores(self):
+        return self.scores[self.S % 2]
+
+    def final_nodes(self):
+        return self.nodes[self.S % 2]

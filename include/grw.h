@@ -1,0 +1,219 @@
+/*
+ * grw.h — C ABI of the wide-beam decode-step library for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of wide-beam generative recommendation:
+ *   beam_select       trie-masked per-beam top_k, then the global beam_width-of-pool select
+ *   beam_attn_decode  beam attention over a shared prompt KV plus per-beam decode KV
+ *                     reached through parent pointers, in three stages
+ *                     (shared stage, unshared stage, online-softmax merge)
+ *
+ * Sources of the operations (cited by page title and section):
+ *   xLLM "generative recommendation design" doc, section 4.1.1 (every beam expands top_k
+ *   candidates; beam_width new beams are chosen from the beam_width x top_k pool),
+ *   section 4.2.1 (prompt KV stored once and shared by all beams; decode-token KV per beam
+ *   at token granularity, no block copy), section 4.2.2 (shared stage, unshared stage,
+ *   OnlineSoftmax merge), section 4.3 (early termination of sorting, early filtering of
+ *   invalid item paths, reuse of candidate containers), section 3.2 (multi-step execution
+ *   with no per-step device-to-host round trip; buffers prepared once up front);
+ *   FlashRec announcement in the SGLang beam-search PR thread (a fused semantic-ID trie,
+ *   dense or CSR, so illegal IDs are never candidates).
+ *
+ * Conventions shared by every entry point
+ *   - Return value: GRW_OK or an error code (grw_status_str gives its text).
+ *   - Every tensor argument is caller-owned DEVICE memory unless stated otherwise; the
+ *     library never frees it.  The library allocates device memory only in grw_ws_create
+ *     (and pinned host staging there); it never allocates in any other call.
+ *   - Every call that takes a stream enqueues its work on that stream and returns
+ *     without synchronising and without any device-to-host copy, except grw_ws_bind_batch
+ *     (one host-to-device upload of descriptors, then a stream synchronise) and
+ *     grw_ws_error (synchronises to read the device flags).
+ *   - Host-checkable argument errors return GRW_EINVAL / GRW_EUNSUPPORTED with nothing
+ *     enqueued.  Device-side precondition violations (a parent or node id out of range,
+ *     NaN or positive log-probabilities) do not stop the kernels; they set bits in a
+ *     device flag word that grw_ws_error reports.
+ *   - A workspace serves one stream at a time; calls on one workspace from two streams
+ *     at once race.
+ *   - Streams are hipStream_t passed as void* (NULL = the default stream).
+ *
+ * Indexing
+ *   A batch holds R requests; request r owns beam slots [boff_r, boff_r + W_r) of
+ *   sumW = sum_r W_r slots (boff_r = W_0 + ... + W_{r-1}).  Requests never mix: every
+ *   selection and every attention read stays inside one request.
+ */
+#ifndef GRW_H
+#define GRW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct grw_ws grw_ws;
+
+enum grw_status {
+  GRW_OK = 0,
+  GRW_EINVAL = 1,        /* bad argument (null pointer, size beyond a limit, mismatch)  */
+  GRW_ENOMEM = 2,        /* device or pinned-host allocation failed in grw_ws_create     */
+  GRW_EDEVICE = 3,       /* a HIP runtime call failed                                    */
+  GRW_EUNSUPPORTED = 4,  /* valid but unsupported shape / dtype combination              */
+  GRW_ESTATE = 5         /* call order: e.g. a step call before grw_ws_bind_batch        */
+};
+
+enum grw_dtype { GRW_F32 = 0, GRW_BF16 = 1, GRW_FP8_E4M3 = 2 };
+
+/* device flag bits reported by grw_ws_error */
+enum grw_device_flag {
+  GRW_FLAG_NAN_LOGPROB = 1,     /* a NaN log-probability or beam score was seen            */
+  GRW_FLAG_POS_LOGPROB = 2,     /* a log-probability > 0 was seen (breaks the early exit)   */
+  GRW_FLAG_BAD_NODE = 4,        /* a live beam's trie node is outside [0, n_internal)       */
+  GRW_FLAG_BAD_PARENT = 8,      /* a parent pointer walk left [0, W_r)                       */
+  GRW_FLAG_CHILD_MISSING = 16   /* a selected code is not a child of its parent's node      */
+};
+
+/*
+ * Limits fixed at workspace creation; every later call is checked against them.
+ *   max_requests     R of any bound batch
+ *   max_total_beams  sumW of any bound batch
+ *   max_W            beam_width of any request (<= 8192)
+ *   max_K            top_k of any request (<= 2048)
+ *   max_C            codes per level / vocabulary of beam_select
+ *   max_S            decode steps (depth of parent_idx / unshared KV), <= 64
+ *   max_P            prompt length of any request
+ *   Hq, Hkv, D       query heads, kv heads (Hq % Hkv == 0, Hq/Hkv in {1,2,4}),
+ *                    head dim; Hkv * D must be one of 128, 256, 512, 1024
+ *   q_dtype          GRW_F32 or GRW_BF16
+ *   kv_dtype         GRW_F32, GRW_BF16 or GRW_FP8_E4M3 (OCP E4M3 "fn")
+ *   max_splits       partial-result slots of the shared stage's split over the prompt
+ *                    (1..16; 0 means 8)
+ */
+typedef struct grw_limits {
+  int32_t max_requests;
+  int32_t max_total_beams;
+  int32_t max_W;
+  int32_t max_K;
+  int32_t max_C;
+  int32_t max_S;
+  int32_t max_P;
+  int32_t Hq, Hkv, D;
+  int32_t q_dtype, kv_dtype;
+  int32_t max_splits;
+} grw_limits;
+
+/* Allocate a workspace (all device buffers the step needs, sized by the limits).
+   The workspace is bound to the device current at the time of the call. */
+int grw_ws_create(const grw_limits* limits, grw_ws** out);
+int grw_ws_destroy(grw_ws* ws);
+
+/*
+ * Bind a batch (setup, once per batch — not per step).
+ *   W_host, K_host, P_host: HOST arrays [n_requests] of beam_width, top_k and prompt
+ *   length per request.  Validated against the limits, then the per-request descriptors
+ *   and the shared-stage work list are uploaded with one host-to-device copy; the call
+ *   synchronises the stream before returning.
+ */
+int grw_ws_bind_batch(grw_ws* ws, int32_t n_requests, const int32_t* W_host,
+                      const int32_t* K_host, const int32_t* P_host, void* stream);
+
+/* Level-0 beam state for the bound batch: slot boff_r of every request gets score 0 and
+   trie node 0 (the root); every other slot gets score -inf and node -1.
+   beam_scores [sumW] float, beam_node [sumW] int32. */
+int grw_beams_init(grw_ws* ws, float* beam_scores, int32_t* beam_node, void* stream);
+
+/*
+ * beam_attn_decode — attention of every beam slot of the bound batch at decode depth
+ * `step`, for one layer (xLLM design doc, sections 4.2.1 and 4.2.2).
+ *
+ * For slot b of request r at depth d = step the beam's key/value sequence is the P_r
+ * prompt tokens followed by its d + 1 decode tokens: the tokens of its ancestors at
+ * depths 0..d-1 and its own token at depth d, found by walking parent pointers
+ * (j_d = b, j_{e-1} = parent_idx[e][boff_r + j_e], request-local slot ids).
+ * Output = softmax(q k^T / sqrt(D)) v per query head; query head h reads kv head
+ * h / (Hq / Hkv).  A slot whose parent_idx[step][slot] is negative is dead: its output
+ * row is zero.
+ *
+ * Three stages run on `stream`: the shared stage (each prompt KV tile streamed once per
+ * beam group into LDS and reused by all of the request's beams, bf16 MFMA when D = 128
+ * and q is bf16), the unshared stage (one wavefront per beam walking parent pointers),
+ * and the online-softmax merge of their partial outputs and log-sum-exp statistics.
+ *
+ *   q          [sumW][Hq][D]  q_dtype
+ *   k_shared   prompt keys of this layer, requests packed back to back: request r's block
+ *              is [Hkv][Pp_r][D] at element offset Hkv*D*(Pp_0 + ... + Pp_{r-1}),
+ *              Pp_r = P_r rounded up to a multiple of 64 (rows >= P_r are ignored)
+ *   v_shared   prompt values of this layer, same packing, each block TRANSPOSED:
+ *              [Hkv][D][Pp_r] (the PV contraction streams it without a transpose)
+ *   k_scale, v_scale  [Hkv] float per-head scales (GRW_FP8_E4M3 only, else NULL); the
+ *              value of an fp8 code is code * scale
+ *   k_unshared, v_unshared  [>= step + 1][sumW][Hkv][D]  kv_dtype: the decode token of
+ *              slot b at depth e is row [e][b]
+ *   parent_idx [>= step + 1][sumW] int32, request-local parent slots; row 0 only marks
+ *              dead slots (negative)
+ *   out        [sumW][Hq][D] float32
+ */
+int beam_attn_decode(grw_ws* ws, const void* q, const void* k_shared, const void* v_shared,
+                     const float* k_scale, const float* v_scale, const void* k_unshared,
+                     const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                     float* out, void* stream);
+
+/*
+ * beam_select — one selection step for every request of the bound batch (xLLM design doc,
+ * sections 4.1.1 and 4.3; FlashRec's trie-constrained expansion).
+ *
+ * For every live slot b (finite beam_scores[b]) of request r, the candidates are the
+ * codes c of the CSR row of its trie node beam_node[b] (every c in [0, C) when the trie
+ * pointers are NULL).  key(b, c) = fl32(beam_scores[b] + logprobs[b][c]); keys equal to
+ * -inf are not candidates.  Each beam keeps its K_r best candidates, the request keeps
+ * the W_r best of that pool; order is key descending, ties by flat index
+ * (b - boff_r) * C + c ascending (+0.0 and -0.0 compare equal).  Output slot i of request
+ * r (global slot boff_r + i) holds the i-th best: token c, parent (b - boff_r), score
+ * key (the exact float32 sum), node = the child of beam_node[b] reached by c (-1 when
+ * unconstrained).  If the pool holds n < W_r candidates, slots n..W_r-1 become pads
+ * (token -1, parent -1, score -inf, node -1).
+ *
+ * Early exit (section 4.3): log-probabilities must be <= 0 (log_softmax output), so no
+ * key exceeds its beam's score; a beam whose score is below a proven lower bound of the
+ * W_r-th best key contributes nothing and is skipped.  The result is the same as
+ * without the exit whenever the precondition holds (GRW_FLAG_POS_LOGPROB reports it).
+ *
+ *   logprobs     [sumW][C] float32, row-major
+ *   beam_scores  [sumW] float32, beam_node [sumW] int32 (ignored when unconstrained)
+ *   trie_row_ptr [n_internal + 1], trie_code [n_edges] int32: breadth-first node ids
+ *                with the root 0, codes ascending within a row, the child reached through
+ *                edge e is node e + 1; both NULL for unconstrained selection
+ *   W, K         must equal the largest W_r and the largest K_r of the bound batch
+ *   C            codes per level (<= max_C); (max W_r) * C must be < 2^32
+ *   out_*        [sumW] each; out_parent may alias a row of parent_idx, out_score and
+ *                out_node must not alias beam_scores / beam_node
+ */
+int beam_select(grw_ws* ws, const float* logprobs, const float* beam_scores,
+                const int32_t* beam_node, const int32_t* trie_row_ptr,
+                const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K,
+                int32_t C, int32_t* out_token, int32_t* out_parent, float* out_score,
+                int32_t* out_node, void* stream);
+
+/*
+ * grw_backtrack — the semantic-ID tuple of every final beam (xLLM design doc, section
+ * 4.1.1: the item id is the fixed-length sequence of generated tokens).
+ *   tokens, parents  [S][sumW] int32, the out_token / out_parent of steps 0..S-1
+ *   sid_out          [sumW][S] int32; sid_out[b][d] is the code chosen at depth d on the
+ *                    path of final slot b (all -1 for a pad slot)
+ */
+int grw_backtrack(grw_ws* ws, const int32_t* tokens, const int32_t* parents, int32_t S,
+                  int32_t* sid_out, void* stream);
+
+/* Synchronise the workspace's last stream and report (then clear) the device flag word
+   (grw_device_flag bits) in *flags (host pointer). */
+int grw_ws_error(grw_ws* ws, void* stream, int32_t* flags);
+
+/* Number of partial-result splits the shared stage uses for request r of the bound batch
+   (diagnostics; host-side, no device work). */
+int grw_ws_splits(const grw_ws* ws, int32_t r, int32_t* n_splits);
+
+const char* grw_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRW_H */

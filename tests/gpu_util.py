@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU parity tests: upload synthetic inputs, drive the library
+through its binding, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle.attention import oracle_attention
+from oracle.select import catalog_prefix_sets, initial_beams, oracle_select
+from synth import build_trie_csr
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_ws(lib, Ws, Ks, Ps, *, C, S, Hq=16, Hkv=8, D=128, q_dtype="bf16", kv_dtype="bf16",
+            max_splits=0):
+    ws = lib.Workspace(max_requests=len(Ws), max_total_beams=int(sum(Ws)), max_W=int(max(Ws)),
+                       max_K=int(max(Ks)), max_C=int(C), max_S=int(S), max_P=int(max(Ps)), Hq=Hq,
+                       Hkv=Hkv, D=D, q_dtype=q_dtype, kv_dtype=kv_dtype, max_splits=max_splits)
+    ws.bind_batch(Ws, Ks, Ps)
+    return ws
+
+
+def trie_device(trie):
+    if trie is None:
+        return None
+    return (torch.from_numpy(trie["row_ptr"]).cuda(), torch.from_numpy(trie["code"]).cuda(),
+            int(trie["n_internal"]))
+
+
+def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label=""):
+    """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
+    every checked request bit-exactly with oracle_select at every step.  Returns the loop."""
+    Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
+    R = len(Ws)
+    boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
+    trie = build_trie_csr(items, C) if items is not None else None
+    psets = catalog_prefix_sets(items, C) if items is not None else None
+    ws = make_ws(lib, Ws, Ks, [64] * R, C=C, S=S)
+    loop = lib.DecodeLoop(ws, S, C, trie_device(trie))
+    ws.beams_init(loop.scores[0], loop.nodes[0])
+    check = list(range(R)) if check is None else list(check)
+    state = {r: initial_beams(Ws[r]) for r in check}
+    for d in range(S):
+        lp = lp_of_step(d)
+        loop.select_step(d, torch.from_numpy(np.ascontiguousarray(lp)).cuda())
+        torch.cuda.synchronize()
+        tok = loop.tokens[d].cpu().numpy()
+        par = loop.parents[d].cpu().numpy()
+        sc = loop.scores[(d + 1) % 2].cpu().numpy()
+        nd = loop.nodes[(d + 1) % 2].cpu().numpy()
+        for r in check:
+            a, W = boff[r], Ws[r]
+            scores, prefixes = state[r]
+            res = oracle_select(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets)
+            where = f"{label} step {d} request {r}"
+            np.testing.assert_array_equal(tok[a:a + W], res["tokens"], err_msg=where + " tokens")
+            np.testing.assert_array_equal(par[a:a + W], res["parents"], err_msg=where + " parents")
+            np.testing.assert_array_equal(sc[a:a + W].view(np.uint32), res["scores"].view(np.uint32),
+                                          err_msg=where + " score bits")
+            n = int((res["parents"] >= 0).sum())
+            if trie is not None:
+                got = trie["node_prefix"][nd[a:a + n]]
+                want = np.array(res["prefixes"][:n], np.int64)
+                np.testing.assert_array_equal(got, want, err_msg=where + " node prefixes")
+                assert np.all(trie["node_depth"][nd[a:a + n]] == d + 1), where
+            else:
+                assert np.all(nd[a:a + W] == -1), where
+            assert np.all(nd[a + n:a + W] == -1), where
+            state[r] = (res["scores"], res["prefixes"])
+    flags = ws.error_flags()
+    assert flags == 0, f"device flags {flags}"
+    return loop, ws
+
+
+def upload_layer(layer, wl_dtype_q, wl_dtype_kv, device="cuda"):
+    """Synthetic layer (synth.attention_layer output) -> device tensors in library layout."""
+    lib_layout = sys.modules["generative_recommendation_wide_amd"]
+    k_s, v_s = lib_layout.pack_shared_kv(layer["k_s"], layer["v_s"], wl_dtype_kv, device)
+    out = dict(q=lib_layout.stored_tensor(layer["q"], wl_dtype_q, device),
+               k_s=k_s, v_s=v_s,
+               k_u=lib_layout.stored_tensor(layer["k_u"], wl_dtype_kv, device),
+               v_u=lib_layout.stored_tensor(layer["v_u"], wl_dtype_kv, device),
+               k_scale=None if layer["k_scale"] is None else torch.from_numpy(layer["k_scale"]).to(device),
+               v_scale=None if layer["v_scale"] is None else torch.from_numpy(layer["v_scale"]).to(device))
+    return out
+
+
+def attention_vs_oracle(out_gpu, layer, parents, step, Ws, q_dtype, kv_dtype, samples, tol, label=""):
+    """Compare sampled slots of the GPU output [sumW][Hq][D] with oracle_attention."""
+    boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
+    worst = 0.0
+    for r, beams in samples.items():
+        a, W = boff[r], Ws[r]
+        beams = list(beams)
+        if not beams:
+            continue
+        ref = oracle_attention(layer["q"][step][a:a + W], layer["k_s"][r], layer["v_s"][r],
+                               layer["k_u"][:, a:a + W], layer["v_u"][:, a:a + W], parents[:, a:a + W],
+                               step, q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=layer["k_scale"],
+                               v_scale=layer["v_scale"], beams=beams)
+        got = out_gpu[a + np.array(beams)].astype(np.float64)
+        err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+        worst = max(worst, err)
+        assert err <= tol, f"{label} request {r}: max abs error {err} > {tol}"
+    return worst

@@ -1,0 +1,120 @@
+"""GPU parity of beam_attn_decode against the oracle's float64 concatenated-KV attention.
+
+Tolerance (max abs error): 1e-4 for float32 inputs, 2e-2 for bf16 / fp8 KV with float32
+accumulation.  Parent pointers are uniform in [0, W_r) per depth, with dead slots."""
+import numpy as np
+import pytest
+import torch
+
+from synth import attention_layer, random_parents, request_shapes, workload
+from tests.gpu_util import attention_vs_oracle, make_ws, say, upload_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 2e-2}
+
+
+def run_attention(lib, wl, layer, parents, Ws, Ks, Ps, steps, samples_of_step, max_splits=0,
+                  Hq=None, Hkv=None, D=None):
+    Hq, Hkv, D = Hq or wl.Hq, Hkv or wl.Hkv, D or wl.D
+    ws = make_ws(lib, Ws, Ks, Ps, C=16, S=wl.S, Hq=Hq, Hkv=Hkv, D=D, q_dtype=wl.q_dtype,
+                 kv_dtype=wl.kv_dtype, max_splits=max_splits)
+    dev = upload_layer(layer, wl.q_dtype, wl.kv_dtype)
+    par = torch.from_numpy(parents).cuda()
+    out = torch.empty(int(sum(Ws)), Hq, D, dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for d in steps:
+        out.fill_(float("nan"))
+        lib.beam_attn_decode(ws, dev["q"][d], dev["k_s"], dev["v_s"], dev["k_scale"], dev["v_scale"],
+                             dev["k_u"], dev["v_u"], par, d, out)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        # dead slots are exactly zero
+        dead = np.nonzero(parents[d] < 0)[0]
+        assert np.all(o[dead] == 0.0)
+        worst = max(worst, attention_vs_oracle(o, layer, parents, d, list(Ws), wl.q_dtype, wl.kv_dtype,
+                                               samples_of_step(d), TOL[wl.kv_dtype], label=f"{wl.name} d={d}"))
+    assert ws.error_flags() == 0
+    say(f"[attn] {wl.name}: worst max-abs error {worst:.3e}")
+    return ws
+
+
+def all_slots(Ws):
+    return lambda d: {r: range(int(w)) for r, w in enumerate(Ws)}
+
+
+def test_tiny_fp32_every_slot(lib):
+    wl = workload("tiny")
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl, dead_frac=0.25)
+    run_attention(lib, wl, layer, par, W, K, P, range(wl.S), all_slots(W))
+
+
+def test_qwen06b_bf16_every_slot(lib):
+    wl = workload("qwen06b")
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl, dead_frac=0.1)
+    ws = run_attention(lib, wl, layer, par, W, K, P, [0, 2], all_slots(W))
+    assert ws.splits(0) > 1          # the prompt is split across workgroups and merged
+
+
+def test_wide512_sampled(lib):
+    wl = workload("wide512")
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl)
+    rng = np.random.default_rng(1)
+    samples = lambda d: {r: rng.choice(512, size=24, replace=False) for r in range(len(W))}
+    run_attention(lib, wl, layer, par, W, K, P, range(wl.S), samples)
+
+
+def test_mixed_fp8_ragged(lib):
+    wl = workload("mixed_fp8")
+    W, K, P = request_shapes(wl)
+    rng = np.random.default_rng(2)
+    check = sorted(set(rng.choice(len(W) - 1, size=10, replace=False).tolist()) | {len(W) - 1})
+    layer = attention_layer(wl, 0, requests=check)
+    # prompt KV of unchecked requests still has to exist on the device: zeros of the right shape
+    for r in range(len(W)):
+        if layer["k_s"][r] is None:
+            layer["k_s"][r] = np.zeros((wl.Hkv, int(P[r]), wl.D), np.uint8)
+            layer["v_s"][r] = np.zeros((wl.Hkv, int(P[r]), wl.D), np.uint8)
+    par = random_parents(wl, dead_frac=0.1)
+    samples = lambda d: {r: (range(int(W[r])) if W[r] <= 8 else rng.choice(int(W[r]), size=8, replace=False))
+                         for r in check}
+    run_attention(lib, wl, layer, par, W, K, P, [0, 3], samples)
+
+
+def test_ultra5000_deep_ancestry(lib):
+    wl = workload("ultra5000")
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl)
+    rng = np.random.default_rng(3)
+    samples = lambda d: {0: rng.choice(5000, size=24, replace=False)}
+    run_attention(lib, wl, layer, par, W, K, P, [0, 7, 15], samples)
+
+
+@pytest.mark.parametrize("P", [1, 63, 65, 1000, 4097])
+def test_ragged_prompt_lengths_and_rows(lib, P):
+    """Prompt lengths off the 64-key tile, row counts off the 128-row tile, split prompts."""
+    import dataclasses
+    wl = dataclasses.replace(workload("qwen06b"), n_requests=3, W=None, K=None, P=None, S=3, index=90 + P)
+    Ws = np.array([1, 37, 70], np.int32)
+    Ps = np.array([P, max(1, P // 2), P + 3], np.int32)
+    Ks = Ws.copy()
+    layer = attention_layer(wl, 0, shapes=(Ws, Ks, Ps))
+    par = random_parents(wl, shapes=(Ws, Ks, Ps), dead_frac=0.2)
+    run_attention(lib, wl, layer, par, Ws, Ks, Ps, [0, 2], all_slots(Ws), max_splits=4)
+
+
+def test_bf16_generic_head_dim_path(lib):
+    """Head dim 64 with bf16 KV takes the generic VALU shared stage."""
+    import dataclasses
+    wl = dataclasses.replace(workload("qwen06b"), n_requests=2, W=9, K=9, P=300, D=64, S=2, index=80)
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl)
+    run_attention(lib, wl, layer, par, W, K, P, [0, 1], all_slots(W))

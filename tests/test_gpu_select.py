@@ -1,0 +1,101 @@
+"""GPU parity of beam_select against the oracle: bit-exact tokens, parents, score bits, order
+and trie nodes, on the synthetic workloads and on edge cases."""
+import numpy as np
+import pytest
+import torch
+
+from synth import catalog_items, logprob_rows, request_shapes, workload
+from tests.gpu_util import say, select_loop_vs_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen06b"])
+def test_workload_every_step(lib, name):
+    wl = workload(name)
+    W, K, P = request_shapes(wl)
+    items = catalog_items(wl)
+    say(f"[select] {name}: R={len(W)} W={W[0]} K={K[0]} C={wl.C}")
+    select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), items, label=name)
+
+
+def test_wide512_zipf_trie(lib):
+    wl = workload("wide512")
+    W, K, P = request_shapes(wl)
+    items = catalog_items(wl)
+    say(f"[select] wide512: {len(items)} items")
+    select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), items,
+                          check=[0, 3], label="wide512")
+
+
+def test_wide512_unconstrained_full_pool(lib):
+    wl = workload("wide512u")
+    W, K, P = request_shapes(wl)
+    say("[select] wide512u")
+    select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), None,
+                          check=[1], label="wide512u")
+
+
+def test_mixed_ragged_batch(lib):
+    wl = workload("mixed_fp8")
+    W, K, P = request_shapes(wl)
+    items = catalog_items(wl)
+    rng = np.random.default_rng(0)
+    check = sorted(set(rng.choice(len(W) - 1, size=12, replace=False).tolist()) | {len(W) - 1})
+    say(f"[select] mixed: R={len(W)} sumW={W.sum()} checking {check}")
+    select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), items, check=check,
+                          label="mixed")
+
+
+def _tie_lp(rng, n, C, values):
+    return rng.choice(np.array(values, np.float32), size=(n, C))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_small_batches_with_ties(lib, seed):
+    """Many small requests in one ragged batch: ties, -0.0, -inf, K > fan-out, pools
+    smaller than W (pads), W = 1 and K = 1."""
+    rng = np.random.default_rng(1000 + seed)
+    C = int(rng.integers(2, 40))
+    L = 3
+    items = np.unique(rng.integers(0, C, size=(int(rng.integers(5, 300)), L)), axis=0)
+    R = 40
+    Ws = rng.integers(1, 12, size=R)
+    Ks = rng.integers(1, 12, size=R)
+    sumW = int(Ws.sum())
+    tie = seed % 2 == 0
+
+    def lp(d):
+        g = np.random.default_rng([seed, d])
+        if tie:
+            return _tie_lp(g, sumW, C, [0.0, -0.0, -0.5, -1.0, -np.inf])
+        return np.minimum(g.standard_normal((sumW, C)).astype(np.float32), 0)
+
+    select_loop_vs_oracle(lib, Ws, Ks, C, L, lp, items, label=f"random{seed}")
+    select_loop_vs_oracle(lib, Ws, Ks, C, L, lp, None, label=f"random{seed}u")
+
+
+def test_long_rows_stream_through_buffer(lib):
+    """Unconstrained rows longer than the LDS buffer, C not a multiple of the chunk:
+    exercises compaction rounds and the admission threshold."""
+    C = 30011
+    Ws, Ks = [7, 33, 5], [3, 64, 200]
+    rng = np.random.default_rng(5)
+    lps = [np.minimum(rng.standard_normal((sum(Ws), C)).astype(np.float32) * 2, 0) for _ in range(3)]
+    select_loop_vs_oracle(lib, Ws, Ks, C, 3, lambda d: lps[d], None, label="long")
+
+
+def test_early_exit_bound_keeps_result(lib):
+    """W = K = 512 over an unconstrained 2048-code level: beams publish lower bounds of the
+    512-th best key and later beams exit early; the result must not change."""
+    C = 2048
+    rng = np.random.default_rng(6)
+    lps = [np.minimum(rng.standard_normal((512, C)).astype(np.float32) * 3 - 6, 0) for _ in range(3)]
+    select_loop_vs_oracle(lib, [512], [512], C, 3, lambda d: lps[d], None, label="bound")
+
+
+def test_wide_tie_plateau(lib):
+    """Many equal keys at the cut: every candidate key equal, so the tie-break alone decides."""
+    C = 700
+    lps = [np.full((300, C), -1.0, np.float32) for _ in range(2)]
+    select_loop_vs_oracle(lib, [300], [250], C, 2, lambda d: lps[d], None, label="plateau")
