@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Throughput of the wide-beam decode step on one MI355X.
+
+One bench step = one pass of the whole hot path over one batch: the device-resident
+S-step decode loop (per decode step: beam_select for every request, then
+beam_attn_decode for every layer), ending with the semantic-ID backtrack.  The reported
+value is beam decode steps per second (S decode steps per bench step).
+
+Default workload "wide512": 4 requests, beam_width = top_k = 512 (262144-candidate pools),
+prompt 4096, 16 query / 8 kv heads, head dim 128, 28 layers, bf16 KV, 3 decode steps over
+8192-code levels constrained by a 4M-item Zipf(1.1) catalog trie.  Inputs are synthetic
+(seeded), generated on the device in the library's storage layout before timing.
+
+Usage:  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide512]
+        python bench.py --summarize DIR   (rocprofv3 output -> profiles/*.md summaries)
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+DOMINANT = "attn_shared_mfma_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_shared_mfma_wide512_traffic.txt")
+KERNEL_SOURCES = ["generative_recommendation_wide_amd/csrc/attn_shared.hip",
+                  "generative_recommendation_wide_amd/csrc/device_common.h",
+                  "generative_recommendation_wide_amd/csrc/grw_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------------------
+# workload setup (device-side synthetic inputs in the library's storage layout)
+# ----------------------------------------------------------------------------------------
+def setup(wl, seed, dev):
+    import numpy as np
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    from synth import build_trie_csr, catalog_items, request_shapes
+
+    W, K, P = request_shapes(wl, seed)
+    sumW, S, C = int(W.sum()), wl.S, wl.C
+    Pp = ((P + 63) // 64) * 64
+    kv_elems = int(wl.Hkv * wl.D * Pp.sum())
+    g = torch.Generator(device=dev).manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32)
+
+    def kv_store(x, scale=None):
+        if wl.kv_dtype == "bf16":
+            return x.to(torch.bfloat16)
+        if wl.kv_dtype == "fp8":
+            return (x / scale).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        return x
+
+    layers = []
+    for _ in range(wl.layers):
+        q = randn(S, sumW, wl.Hq, wl.D).to(torch.bfloat16 if wl.q_dtype == "bf16" else torch.float32)
+        ks, vs = randn(kv_elems), randn(kv_elems)
+        ku, vu = randn(S, sumW, wl.Hkv, wl.D), randn(S, sumW, wl.Hkv, wl.D)
+        k_scale = v_scale = None
+        if wl.kv_dtype == "fp8":
+            # per kv head scales (amax / 448) over this layer's prompt and decode KV
+            def head_amax(flat, u):
+                m = u.abs().amax(dim=(0, 1, 3))
+                off = 0
+                for p in Pp.tolist():
+                    blk = flat[off:off + wl.Hkv * p * wl.D].view(wl.Hkv, -1).abs().amax(dim=1)
+                    m = torch.maximum(m, blk)
+                    off += wl.Hkv * p * wl.D
+                return m
+            k_scale = (head_amax(ks, ku) / 448.0).float()
+            v_scale = (head_amax(vs, vu) / 448.0).float()
+            # broadcast scale over the packed layout: [Hkv][...] blocks per request
+            def scale_flat(x, sc):
+                out, off = [], 0
+                for p in Pp.tolist():
+                    n = wl.Hkv * p * wl.D
+                    out.append(kv_store(x[off:off + n].view(wl.Hkv, -1), sc[:, None]).reshape(-1))
+                    off += n
+                return torch.cat(out)
+            ks_s, vs_s = scale_flat(ks, k_scale), scale_flat(vs, v_scale)
+            ku_s = kv_store(ku, k_scale[None, None, :, None])
+            vu_s = kv_store(vu, v_scale[None, None, :, None])
+        else:
+            ks_s, vs_s, ku_s, vu_s = kv_store(ks), kv_store(vs), kv_store(ku), kv_store(vu)
+        layers.append(dict(q=q, k_s=ks_s, v_s=vs_s, k_u=ku_s, v_u=vu_s, k_scale=k_scale, v_scale=v_scale))
+        del ks, vs, ku, vu
+    lps = []
+    for _ in range(S):
+        x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
+        lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
+        del x
+    trie = None
+    items = catalog_items(wl, seed)
+    if items is not None:
+        t = build_trie_csr(items, C)
+        trie = (torch.from_numpy(t["row_ptr"]).to(dev), torch.from_numpy(t["code"]).to(dev), t["n_internal"])
+    ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
+                       max_C=C, max_S=S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                       q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
+    ws.bind_batch(W, K, P)
+    loop = grw.DecodeLoop(ws, S, C, trie, device=dev)
+    out = torch.empty(sumW, wl.Hq, wl.D, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    return dict(W=W, K=K, P=P, ws=ws, loop=loop, layers=layers, lps=lps, out=out, trie=trie)
+
+
+def shared_stage_work(wl, st):
+    """Algorithmic flops and bytes of one shared-stage launch (one layer, all requests)."""
+    W, P = st["W"], st["P"]
+    ws = st["ws"]
+    esz = {"bf16": 2, "fp8": 1, "f32": 4}[wl.kv_dtype]
+    qsz = 2 if wl.q_dtype == "bf16" else 4
+    flops = sum(4.0 * int(W[r]) * wl.Hq * int(P[r]) * wl.D for r in range(len(W)))
+    bytes_ = sum(2.0 * wl.Hkv * int(P[r]) * wl.D * esz            # K and V prompt tiles, once
+                 + int(W[r]) * wl.Hq * wl.D * qsz                 # queries
+                 + ws.splits(r) * int(W[r]) * wl.Hq * (wl.D + 1) * 4   # partial o + lse
+                 for r in range(len(W)))
+    return flops, bytes_
+
+
+def time_stage(fn, n_launch, stream):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()                                   # warm
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_launch):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_launch   # ms per call
+
+
+def stage_timings(wl, st, reps):
+    """Per-call device time of each stage, HIP events on the launch stream."""
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    stream = torch.cuda.current_stream()
+    loop, layers, out, ws = st["loop"], st["layers"], st["out"], st["ws"]
+    d = wl.S - 1
+    calls = [(li, d) for li in range(len(layers))]
+    res = {}
+    for name, mask in (("shared", grw.STAGE_SHARED), ("unshared", grw.STAGE_UNSHARED), ("merge", grw.STAGE_MERGE)):
+        it = iter(range(10 ** 9))
+
+        def fn(mask=mask):
+            li, dd = calls[next(it) % len(calls)]
+            L = layers[li]
+            grw.beam_attn_decode_stages(ws, L["q"][dd], L["k_s"], L["v_s"], L["k_scale"], L["v_scale"],
+                                        L["k_u"], L["v_u"], loop.parents, dd, out, mask)
+        res[name] = time_stage(fn, reps * len(calls), stream)
+
+    def sel_all():
+        ws.beams_init(loop.scores[0], loop.nodes[0])
+        for dd in range(wl.S):
+            loop.select_step(dd, st["lps"][dd])
+    res["select_loop_3steps"] = time_stage(sel_all, reps, stream)
+    return res
+
+
+# ----------------------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample of the same workload
+# ----------------------------------------------------------------------------------------
+def cpu_baseline(wl, seed):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import oracle_attention
+    from oracle.select import catalog_prefix_sets, initial_beams, oracle_select
+    from synth import attention_layer, catalog_items, logprob_rows, random_parents, request_shapes
+
+    W, K, P = request_shapes(wl, seed)
+    R, W0, K0 = len(W), int(W[0]), int(K[0])
+    items = catalog_items(wl, seed)
+    psets = catalog_prefix_sets(items, wl.C) if items is not None else None
+    with threadpool_limits(limits=1):
+        # selection: request 0, every step (its own parents), timed
+        t_sel = 0.0
+        scores, prefixes = initial_beams(W0)
+        for d in range(wl.S):
+            lp = logprob_rows(wl, d, seed, rows=np.arange(W0))
+            t0 = time.perf_counter()
+            res = oracle_select(lp, scores, prefixes, d, K0, W0, wl.C, psets)
+            t_sel += time.perf_counter() - t0
+            scores, prefixes = res["scores"], res["prefixes"]
+        # attention: a few beams of request 0, layer 0, deepest step
+        layer = attention_layer(wl, 0, seed, requests=[0])
+        par = random_parents(wl, seed)
+        nb = 6
+        d = wl.S - 1
+        t0 = time.perf_counter()
+        oracle_attention(layer["q"][d][:W0], layer["k_s"][0], layer["v_s"][0], layer["k_u"][:, :W0],
+                         layer["v_u"][:, :W0], par[:, :W0], d, q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
+                         k_scale=layer["k_scale"], v_scale=layer["v_scale"], beams=range(nb))
+        t_attn_beam = (time.perf_counter() - t0) / nb
+    sumW = int(W.sum())
+    t_step = R * t_sel / wl.S + sumW * wl.layers * t_attn_beam
+    return {"value": 1.0 / t_step, "unit": "beam decode steps/s", "cores": 1, "kind": "oracle",
+            "sample": (f"oracle_select on request 0 for all {wl.S} steps ({t_sel:.2f} s) and "
+                       f"oracle_attention on {nb} beams of request 0, layer 0, depth {d} "
+                       f"({t_attn_beam * 1e3:.0f} ms/beam); scaled to {R} requests x {sumW} beams "
+                       f"x {wl.layers} layers per decode step; BLAS limited to 1 thread")}
+
+
+def read_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------------------
+# rocprofv3 summaries
+# ----------------------------------------------------------------------------------------
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:                      # drop the parameter list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def summarize(args):
+    """Turn rocprofv3 CSV output into short text summaries under profiles/."""
+    import csv
+    d = args.summarize
+    out_lines = []
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        out_lines.append(f"## kernel stats ({os.path.relpath(f, d)})\n")
+        out_lines.append("| kernel | calls | total ms | avg us | min us | max us | % |")
+        out_lines.append("|---|---|---|---|---|---|---|")
+        for r in rows:
+            short = _short_kernel_name(r.get("Name", ""))
+            out_lines.append(f"| {short[:80]} | {r.get('Calls')} | {float(r.get('TotalDurationNs', 0)) / 1e6:.3f} | "
+                             f"{float(r.get('AverageNs', 0)) / 1e3:.2f} | {float(r.get('MinNs', 0)) / 1e3:.2f} | "
+                             f"{float(r.get('MaxNs', 0)) / 1e3:.2f} | {float(r.get('Percentage', 0)):.2f} |")
+    counters = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    agg = {}
+    for f in counters:
+        for r in csv.DictReader(open(f)):
+            name = _short_kernel_name(r.get("Kernel_Name", ""))
+            key = (name, r.get("Counter_Name"))
+            a = agg.setdefault(key, [0.0, 0])
+            a[0] += float(r.get("Counter_Value", 0))
+            a[1] += 1
+    if agg:
+        out_lines.append("\n## counters (per dispatch average)\n")
+        out_lines.append("| kernel | counter | dispatches | avg value |")
+        out_lines.append("|---|---|---|---|")
+        for (k, c), (s, n) in sorted(agg.items()):
+            out_lines.append(f"| {k[:80]} | {c} | {n} | {s / n:.1f} |")
+    text = "\n".join(out_lines) + "\n"
+    if args.summary_out:
+        with open(args.summary_out, "w") as f:
+            f.write(args.summary_header.replace("\\n", "\n") + "\n" + text if args.summary_header else text)
+    print(text)
+
+
+# ----------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wide512")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=3)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--summarize", default=None)
+    ap.add_argument("--summary-out", default=None)
+    ap.add_argument("--summary-header", default="")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode step shards by request, with no exchange, and multi-GPU runs are not "
+              "part of this build", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from synth import workload
+    wl = workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] setting up {wl.name} ...")
+    t_setup = time.perf_counter()
+    st = setup(wl, args.seed, dev)
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; warmup {args.warmup}, timed {args.steps}")
+    loop, layers, out, lps = st["loop"], st["layers"], st["out"], st["lps"]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        loop.run(lps, layers, out)
+    torch.cuda.synchronize()
+    flags = st["ws"].error_flags()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        loop.run(lps, layers, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = e0.elapsed_time(e1) / 1000.0
+    log(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms")
+    decode_steps = wl.S * args.steps
+    value = decode_steps / wall
+
+    stages = stage_timings(wl, st, args.stage_reps)
+    log(f"[bench] stage ms/call: {stages}")
+    flops, bytes_ = shared_stage_work(wl, st)
+    t_shared = stages["shared"] / 1e3
+    achieved = flops / t_shared / 1e12
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": DOMINANT, "flops_per_launch": flops, "avg_launch_us": round(t_shared * 1e6, 2),
+                "algorithmic_bytes_per_launch": bytes_,
+                "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1)}
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl, args.seed)
+    res = {
+        "metric": "beam decode steps/s (attn+select) at W=K=512; achieved HBM GB/s vs peak",
+        "value": round(value, 2),
+        "unit": "beam decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.kv_dtype == "bf16" else wl.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "requests": len(st["W"]), "beam_width": int(st["W"].max()),
+                   "top_k": int(st["K"].max()), "prompt": int(st["P"].max()), "layers": wl.layers,
+                   "heads": f"{wl.Hq}/{wl.Hkv}x{wl.D}", "codes_per_level": wl.C,
+                   "decode_steps_per_bench_step": wl.S,
+                   "trie": None if wl.catalog is None else f"{wl.catalog[0]} {wl.catalog[1]} items",
+                   "device_flags": flags},
+        "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -12,7 +12,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING, FLAG_NAN_LOGPROB,  # noqa: F401
+from ._lib import (STAGE_MERGE, STAGE_SHARED, STAGE_UNSHARED,  # noqa: F401
+                   FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING, FLAG_NAN_LOGPROB,  # noqa: F401
                    FLAG_POS_LOGPROB, GRW_BF16, GRW_F32, GRW_FP8_E4M3, GrwError, GrwLimits)
 
 _L = _lib.load()
@@ -101,6 +102,17 @@ def beam_attn_decode(ws: Workspace, q, k_shared, v_shared, k_scale, v_scale, k_u
         _ptr(v_shared, _ANY_KV, "v_shared"), _ptr(k_scale, _F32, "k_scale"), _ptr(v_scale, _F32, "v_scale"),
         _ptr(k_unshared, _ANY_KV, "k_unshared"), _ptr(v_unshared, _ANY_KV, "v_unshared"),
         _ptr(parent_idx, _I32, "parent_idx"), int(step), _ptr(out, _F32, "out"), _stream(stream)))
+
+
+def beam_attn_decode_stages(ws: Workspace, q, k_shared, v_shared, k_scale, v_scale, k_unshared,
+                            v_unshared, parent_idx, step: int, out, stages: int, stream=None):
+    """beam_attn_decode restricted to the stages in the bit mask (1 shared, 2 unshared, 4 merge)."""
+    _lib.check("beam_attn_decode_stages", _L.beam_attn_decode_stages(
+        ws.handle, _ptr(q, (torch.float32, torch.bfloat16), "q"), _ptr(k_shared, _ANY_KV, "k_shared"),
+        _ptr(v_shared, _ANY_KV, "v_shared"), _ptr(k_scale, _F32, "k_scale"), _ptr(v_scale, _F32, "v_scale"),
+        _ptr(k_unshared, _ANY_KV, "k_unshared"), _ptr(v_unshared, _ANY_KV, "v_unshared"),
+        _ptr(parent_idx, _I32, "parent_idx"), int(step), _ptr(out, _F32, "out"), int(stages),
+        _stream(stream)))
 
 
 def beam_select(ws: Workspace, logprobs, beam_scores, beam_node, trie_row_ptr, trie_code,

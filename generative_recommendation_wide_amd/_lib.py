@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(HERE, "libgrw.so")
 GRW_OK, GRW_EINVAL, GRW_ENOMEM, GRW_EDEVICE, GRW_EUNSUPPORTED, GRW_ESTATE = range(6)
 GRW_F32, GRW_BF16, GRW_FP8_E4M3 = 0, 1, 2
 FLAG_NAN_LOGPROB, FLAG_POS_LOGPROB, FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING = 1, 2, 4, 8, 16
+STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
-            "beam_attn_decode", "beam_select", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
+            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
             "grw_status_str"]
 
 
@@ -43,7 +44,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m generative_recommendation_wide_amd.build`")
+                          "`python generative_recommendation_wide_amd/build.py`")
     lib = ctypes.CDLL(path)
     vp, i32, i32p, fp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
     sig = {
@@ -52,6 +53,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "grw_ws_bind_batch": [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32), vp],
         "grw_beams_init": [vp, fp, i32p, vp],
         "beam_attn_decode": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, vp],
+        "beam_attn_decode_stages": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, i32, vp],
         "beam_select": [vp, fp, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp, i32p, vp],
         "grw_backtrack": [vp, i32p, i32p, i32, i32p, vp],
         "grw_ws_error": [vp, vp, ctypes.POINTER(i32)],

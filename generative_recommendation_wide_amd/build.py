@@ -1,6 +1,8 @@
 """Build the HIP library libgrw.so in-tree for gfx950.
 
-    python -m generative_recommendation_wide_amd.build
+    python generative_recommendation_wide_amd/build.py
+
+(run it by path: importing the package loads the library this script builds)
 
 Every source is compiled with hipcc for gfx950 only, with packed-FP32 instruction
 selection disabled, then linked into one shared library next to this file.

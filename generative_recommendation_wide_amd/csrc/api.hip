@@ -320,7 +320,16 @@ int beam_attn_decode(grw_ws* w, const void* q, const void* k_shared, const void*
                      const float* k_scale, const float* v_scale, const void* k_unshared,
                      const void* v_unshared, const int32_t* parent_idx, int32_t step,
                      float* out, void* stream) {
+  return beam_attn_decode_stages(w, q, k_shared, v_shared, k_scale, v_scale, k_unshared, v_unshared,
+                                 parent_idx, step, out, 7, stream);
+}
+
+int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, const void* v_shared,
+                            const float* k_scale, const float* v_scale, const void* k_unshared,
+                            const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                            float* out, int32_t stages, void* stream) {
   if (!w) return GRW_EINVAL;
+  if (stages < 1 || stages > 7) return GRW_EINVAL;
   if (!w->bound) return GRW_ESTATE;
   const grw_limits& L = w->lim;
   if (!q || !k_shared || !v_shared || !k_unshared || !v_unshared || !parent_idx || !out)
@@ -354,10 +363,12 @@ int beam_attn_decode(grw_ws* w, const void* q, const void* k_shared, const void*
   a.q_dtype = L.q_dtype;
   a.kv_dtype = L.kv_dtype;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = w->mfma ? launch_attn_shared_mfma(a, w->d_work, w->n_work, s)
-                         : launch_attn_shared_valu(a, w->d_work, w->n_work, s);
-  if (e == hipSuccess) e = launch_attn_unshared(a, s);
-  if (e == hipSuccess) e = launch_attn_merge(a, s);
+  hipError_t e = hipSuccess;
+  if (stages & GRW_STAGE_SHARED)
+    e = w->mfma ? launch_attn_shared_mfma(a, w->d_work, w->n_work, s)
+                : launch_attn_shared_valu(a, w->d_work, w->n_work, s);
+  if (e == hipSuccess && (stages & GRW_STAGE_UNSHARED)) e = launch_attn_unshared(a, s);
+  if (e == hipSuccess && (stages & GRW_STAGE_MERGE)) e = launch_attn_merge(a, s);
   return hip_status(e);
 }
 

@@ -157,6 +157,21 @@ int beam_attn_decode(grw_ws* ws, const void* q, const void* k_shared, const void
                      float* out, void* stream);
 
 /*
+ * beam_attn_decode_stages — beam_attn_decode restricted to a subset of its stages, for
+ * per-stage measurement and testing.  `stages` is a bit mask: GRW_STAGE_SHARED (1) runs the
+ * shared stage (partials into the workspace), GRW_STAGE_UNSHARED (2) the unshared stage,
+ * GRW_STAGE_MERGE (4) the merge into `out`.  The merge reads the partials the other two
+ * stages last wrote into this workspace.  Mask 7 is beam_attn_decode.  Arguments and
+ * errors as for beam_attn_decode; a mask outside 1..7 is GRW_EINVAL.
+ */
+enum grw_stage { GRW_STAGE_SHARED = 1, GRW_STAGE_UNSHARED = 2, GRW_STAGE_MERGE = 4 };
+int beam_attn_decode_stages(grw_ws* ws, const void* q, const void* k_shared,
+                            const void* v_shared, const float* k_scale, const float* v_scale,
+                            const void* k_unshared, const void* v_unshared,
+                            const int32_t* parent_idx, int32_t step, float* out,
+                            int32_t stages, void* stream);
+
+/*
  * beam_select — one selection step for every request of the bound batch (xLLM design doc,
  * sections 4.1.1 and 4.3; FlashRec's trie-constrained expansion).
  *

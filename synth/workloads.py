@@ -14,6 +14,7 @@ Nothing in this module computes attention or selects beams.
 from __future__ import annotations
 
 import dataclasses
+import functools
 from typing import Optional
 
 import numpy as np
@@ -122,6 +123,7 @@ def _first_distinct(draws: np.ndarray, n: int):
     return draws[order]
 
 
+@functools.lru_cache(maxsize=4)
 def catalog_items(wl: Workload, seed: int = 0) -> Optional[np.ndarray]:
     """Distinct items as an int32 array [N, S] of per-level codes, or None if unconstrained.
 

@@ -21,8 +21,8 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def clib():
     if not os.path.exists(LIB):
-        from generative_recommendation_wide_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     return ctypes.CDLL(LIB)
 
 
