@@ -165,7 +165,9 @@ def stage_timings(wl, st, reps):
     d = wl.S - 1
     calls = [(li, d) for li in range(len(layers))]
     res = {}
-    for name, mask in (("shared", grw.STAGE_SHARED), ("unshared", grw.STAGE_UNSHARED), ("merge", grw.STAGE_MERGE)):
+    for name, mask in (("shared", grw.STAGE_SHARED),
+                       ("unshared_merge_fused", grw.STAGE_UNSHARED | grw.STAGE_MERGE),
+                       ("unshared", grw.STAGE_UNSHARED), ("merge", grw.STAGE_MERGE)):
         it = iter(range(10 ** 9))
 
         def fn(mask=mask):
@@ -296,6 +298,52 @@ def summarize(args):
     print(text)
 
 
+def write_traffic(args):
+    """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for the
+    calibration copy (the largest copyBuffer dispatch, of --calib-copy-mib MiB)."""
+    import csv
+    fetch_dir, write_dir = args.traffic
+    calib_kib = args.calib_copy_mib * 1024.0
+
+    def per_dispatch(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        dom, copies = [], []
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if DOMINANT in r["Kernel_Name"]:
+                dom.append(v)
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copies.append(v)
+        return sum(dom) / len(dom), max(copies)
+
+    fk, fcal = per_dispatch(fetch_dir, "FETCH_SIZE")
+    wk, wcal = per_dispatch(write_dir, "WRITE_SIZE")
+    ff, wf = calib_kib / fcal, calib_kib / wcal
+    total = (fk * ff + wk * wf) * 1024.0
+    lines = [
+        f"# HBM traffic of {DOMINANT} per launch (wide512: one layer, 4 requests, W=K=512, P=4096)",
+        "# Commands (repo root on the GPU box, TMPDIR=/tmp), one counter per run:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d $GRAFT_REPO_ROOT/gpurun_out/pmc_fetch -o run --output-format csv -- "
+        f"python $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 1 --stage-reps 0 --no-cpu-baseline --calib-copy-mib {args.calib_copy_mib}",
+        "#   (same with --pmc WRITE_SIZE -d .../pmc_write)",
+        f"#   python bench.py --traffic gpurun_out/pmc_fetch gpurun_out/pmc_write --calib-copy-mib {args.calib_copy_mib}",
+        f"# calibration: a {args.calib_copy_mib} MiB device copy reads FETCH_SIZE={fcal:.1f} KiB and WRITE_SIZE={wcal:.1f} KiB,",
+        f"# so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f}.",
+        f"fetch_kib_raw={fk:.1f}",
+        f"write_kib_raw={wk:.1f}",
+        f"fetch_scale={ff:.4f}",
+        f"write_scale={wf:.4f}",
+        f"hbm_bytes_per_launch={total:.0f}",
+        f"source_sha={kernel_source_sha()}",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ----------------------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -309,11 +357,15 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     ap.add_argument("--summarize", default=None)
+    ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--summary-header", default="")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
+        return 0
+    if args.traffic:
+        write_traffic(args)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -352,7 +404,11 @@ def main():
     decode_steps = wl.S * args.steps
     value = decode_steps / wall
 
-    stages = stage_timings(wl, st, args.stage_reps)
+    if args.stage_reps > 0:
+        stages = stage_timings(wl, st, args.stage_reps)
+    else:
+        stages = {"shared": float("nan"), "unshared_merge_fused": float("nan"), "unshared": float("nan"),
+                  "merge": float("nan"), "select_loop_3steps": float("nan")}
     log(f"[bench] stage ms/call: {stages}")
     flops, bytes_ = shared_stage_work(wl, st)
     t_shared = stages["shared"] / 1e3

@@ -37,9 +37,14 @@ def flags():
             "-I", os.path.join(HERE, "..", "include")]
 
 
+# per-file extra flags: the attention kernels never see NaN (finite bf16 / fp8 / fp32 inputs),
+# so max operations need no NaN quieting; infinities (used for masking) keep IEEE semantics
+EXTRA = {"attn_shared.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -367,8 +367,13 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
   if (stages & GRW_STAGE_SHARED)
     e = w->mfma ? launch_attn_shared_mfma(a, w->d_work, w->n_work, s)
                 : launch_attn_shared_valu(a, w->d_work, w->n_work, s);
-  if (e == hipSuccess && (stages & GRW_STAGE_UNSHARED)) e = launch_attn_unshared(a, s);
-  if (e == hipSuccess && (stages & GRW_STAGE_MERGE)) e = launch_attn_merge(a, s);
+  const int um = stages & (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE);
+  if (e == hipSuccess && um == (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE)) {
+    e = launch_attn_unshared_merge(a, s);        // merge fused into the unshared epilogue
+  } else {
+    if (e == hipSuccess && (stages & GRW_STAGE_UNSHARED)) e = launch_attn_unshared(a, s);
+    if (e == hipSuccess && (stages & GRW_STAGE_MERGE)) e = launch_attn_merge(a, s);
+  }
   return hip_status(e);
 }
 

@@ -25,27 +25,28 @@ constexpr int NT = kShKeys;            // 64 keys per tile
 constexpr int KS = DH + 8;             // LDS row stride (bf16) of the K tile: 272 B
 constexpr int VS = NT + 4;             // LDS row stride (bf16) of the V^T tile: 136 B
 constexpr int K_TILE = NT * KS;        // bf16 elements
+constexpr float kRescale = 8.0f;       // lazy-rescale margin of the running max (log2 units)
 constexpr int V_TILE = DH * VS;
 
+// Register staging of one tile on its way from global memory to LDS.
+// bf16: K 4 x 16 B per thread, V^T 4 x 16 B; fp8: 2 + 2 x 16 B (widened to bf16 on store).
 template <bool FP8>
-struct TileRegs {
-  // bf16: K 4 x 16 B, V^T 4 x 16 B per thread; fp8: 2 + 2 x 16 B
-  static constexpr int N = FP8 ? 2 : 4;
-  u32x4 k[N];
-  u32x4 v[N];
+struct KRegs {
+  u32x4 k[FP8 ? 2 : 4];
+};
+template <bool FP8>
+struct VRegs {
+  u32x4 v[FP8 ? 2 : 4];
 };
 
 template <bool FP8>
-__device__ __forceinline__ void load_tile(TileRegs<FP8>& t, const uint8_t* kb, const uint8_t* vb,
-                                          int p, int Pp, int tid) {
+__device__ __forceinline__ void load_k(KRegs<FP8>& t, const uint8_t* kb, int p, int tid) {
   if constexpr (!FP8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       const int key = c >> 4, dc = c & 15;   // 16 chunks of 8 bf16 per key row
       t.k[i] = *(const u32x4*)(kb + ((size_t)(p + key) * DH + dc * 8) * 2);
-      const int d = c >> 3, kc = c & 7;      // 8 chunks of 8 keys per V^T row
-      t.v[i] = *(const u32x4*)(vb + ((size_t)d * Pp + p + kc * 8) * 2);
     }
   } else {
 #pragma unroll
@@ -53,6 +54,23 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& t, const uint8_t* kb, c
       const int c = tid + 256 * i;
       const int key = c >> 3, dc = c & 7;    // 8 chunks of 16 codes per key row
       t.k[i] = *(const u32x4*)(kb + (size_t)(p + key) * DH + dc * 16);
+    }
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void load_v(VRegs<FP8>& t, const uint8_t* vb, int p, int Pp, int tid) {
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int d = c >> 3, kc = c & 7;      // 8 chunks of 8 keys per V^T row
+      t.v[i] = *(const u32x4*)(vb + ((size_t)d * Pp + p + kc * 8) * 2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
       const int d = c >> 2, kc = c & 3;      // 4 chunks of 16 codes per V^T row
       t.v[i] = *(const u32x4*)(vb + (size_t)d * Pp + p + kc * 16);
     }
@@ -60,17 +78,13 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& t, const uint8_t* kb, c
 }
 
 template <bool FP8>
-__device__ __forceinline__ void store_tile(const TileRegs<FP8>& t, __bf16* sk, __bf16* sv, int tid) {
+__device__ __forceinline__ void store_k(const KRegs<FP8>& t, __bf16* sk, int tid) {
   if constexpr (!FP8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
       const int key = c >> 4, dc = c & 15;
       *(u32x4*)(sk + key * KS + dc * 8) = t.k[i];
-      const int d = c >> 3, kc = c & 7;
-      u32x2* dst = (u32x2*)(sv + d * VS + kc * 8);   // rows are 8-byte aligned
-      dst[0] = u32x2{t.v[i].x, t.v[i].y};
-      dst[1] = u32x2{t.v[i].z, t.v[i].w};
     }
   } else {
 #pragma unroll
@@ -82,6 +96,25 @@ __device__ __forceinline__ void store_tile(const TileRegs<FP8>& t, __bf16* sk, _
       u32x4* kd = (u32x4*)(sk + key * KS + dc * 16);
       kd[0] = u32x4{a.x, a.y, b.x, b.y};
       kd[1] = u32x4{e.x, e.y, f.x, f.y};
+    }
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void store_v(const VRegs<FP8>& t, __bf16* sv, int tid) {
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int d = c >> 3, kc = c & 7;
+      u32x2* dst = (u32x2*)(sv + d * VS + kc * 8);   // rows are 8-byte aligned
+      dst[0] = u32x2{t.v[i].x, t.v[i].y};
+      dst[1] = u32x2{t.v[i].z, t.v[i].w};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
       const int d = c >> 2, kc = c & 3;
       u32x2* vd = (u32x2*)(sv + d * VS + kc * 16);
       vd[0] = fp8x4_to_bf16x4(t.v[i].x);
@@ -89,6 +122,20 @@ __device__ __forceinline__ void store_tile(const TileRegs<FP8>& t, __bf16* sk, _
       vd[2] = fp8x4_to_bf16x4(t.v[i].z);
       vd[3] = fp8x4_to_bf16x4(t.v[i].w);
     }
+  }
+}
+
+// S^T = K Q^T for one 64-key tile: two 32-key blocks of 32 queries.
+__device__ __forceinline__ void tile_scores(const __bf16* kt, const bf16x8 (&qf)[DH / 16], int l32, int hi,
+                                            floatx16& s0, floatx16& s1) {
+  s0 = floatx16{};
+  s1 = floatx16{};
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) {
+    const bf16x8 a0 = *(const bf16x8*)(kt + l32 * KS + ks * 16 + hi * 8);
+    const bf16x8 a1 = *(const bf16x8*)(kt + (32 + l32) * KS + ks * 16 + hi * 8);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
   }
 }
 
@@ -146,13 +193,17 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
   const int p0 = wk.p0, p1 = wk.p1;
   const int ntiles = (p1 - p0 + NT - 1) / NT;
 
-  // LDS: K tiles [2][NT][KS], then V^T tiles [2][DH][VS]
+  // LDS: K tiles [2][NT][KS], then V^T tiles [2][DH][VS], double buffered: tile t+1 is
+  // fetched into registers while tile t is consumed, then stored to the other buffer.
   __bf16* const sk0 = smem;
   __bf16* const sv0 = smem + 2 * K_TILE;
 
-  TileRegs<FP8> regs;
-  load_tile<FP8>(regs, kb, vb, p0, rd.Pp, tid);
-  store_tile<FP8>(regs, sk0, sv0, tid);
+  KRegs<FP8> kr;
+  VRegs<FP8> vr;
+  load_k<FP8>(kr, kb, p0, tid);
+  load_v<FP8>(vr, vb, p0, rd.Pp, tid);
+  store_k<FP8>(kr, sk0, tid);
+  store_v<FP8>(vr, sv0, tid);
   __syncthreads();
 
   float m_run = -INFINITY;   // running max of scaled scores (identical on both lane halves)
@@ -165,18 +216,14 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
     const int buf = t & 1;
     const int p = p0 + t * NT;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile<FP8>(regs, kb, vb, p + NT, rd.Pp, tid);
-
-    // S^T (64 keys x 32 queries) in two 32-key blocks
-    floatx16 s0 = floatx16{}, s1 = floatx16{};
-    const __bf16* kt = sk0 + buf * K_TILE;
-#pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
-      const bf16x8 a0 = *(const bf16x8*)(kt + l32 * KS + ks * 16 + hi * 8);
-      const bf16x8 a1 = *(const bf16x8*)(kt + (32 + l32) * KS + ks * 16 + hi * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+    if (more) {
+      load_k<FP8>(kr, kb, p + NT, tid);
+      load_v<FP8>(vr, vb, p + NT, rd.Pp, tid);
     }
+    floatx16 s0, s1;
+    __builtin_amdgcn_s_setprio(1);
+    tile_scores(sk0 + buf * K_TILE, qf, l32, hi, s0, s1);
+    __builtin_amdgcn_s_setprio(0);
     // value k of block kb belongs to key p + kb*32 + (k/4)*8 + hi*4 + k%4
     if (p + NT > p1) {
 #pragma unroll
@@ -189,29 +236,42 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s0[k], s1[k]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);   // m_run = -inf -> 0
-    float psum = 0.0f;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    // Lazy rescale: the running max m_run only moves when some row's tile max exceeds it
+    // by more than kRescale (log2 units), so p = 2^(s*c - m_run) <= 2^kRescale and the
+    // O / l rescale runs on a few tiles only (wave-uniform branch).
+    if (__any(mx > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);   // m_run = -inf -> 0
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      s0[k] = fast_exp2(fmaf(s0[k], c, -m_new));
-      s1[k] = fast_exp2(fmaf(s1[k], c, -m_new));
-      psum += s0[k] + s1[k];
+      s0[k] = fast_exp2(fmaf(s0[k], c, -m_run));
+      s1[k] = fast_exp2(fmaf(s1[k], c, -m_run));
     }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DH / 32; ++db) o[db] *= alpha;
-
     // P^T fragments: k-step ks covers 16 keys; lane half `hi` supplies its 8 values
     bf16x8 pb[4];
     pb[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
     pb[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
     pb[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
     pb[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+    // row sum of the bf16-rounded P (the values the PV product uses), two per instruction
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 0, 1), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 2, 3), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 4, 5), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 6, 7), ones, l_run, false);
+    }
 
+    // O^T += V^T P^T
     const __bf16* vt = sv0 + buf * V_TILE;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb0 = (ks >> 1) * 32 + (ks & 1) * 16 + hi * 4;   // first key of the lane's run
@@ -224,8 +284,12 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
-    if (more) store_tile<FP8>(regs, sk0 + (buf ^ 1) * K_TILE, sv0 + (buf ^ 1) * V_TILE, tid);
+    if (more) {
+      store_k<FP8>(kr, sk0 + (buf ^ 1) * K_TILE, tid);
+      store_v<FP8>(vr, sv0 + (buf ^ 1) * V_TILE, tid);
+    }
     __syncthreads();
   }
 

@@ -12,6 +12,9 @@
 // Merge: per (slot, query head) the partials i (the shared stage's splits and the
 // unshared stage) combine as lse = log sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i
 // (online-softmax merge).  Dead slots (negative parent pointer at this depth) get zeros.
+// The merge runs either as its own kernel over partials in the workspace, or fused into
+// the unshared kernel's epilogue (the default path), where the unshared partial never
+// leaves registers.
 #include "device_common.h"
 #include "grw_internal.h"
 
@@ -65,7 +68,9 @@ __device__ __forceinline__ void load_row(const void* base, size_t off, float (&x
   }
 }
 
-template <int KVT, int E, int G>
+// FUSE: merge the unshared partial with the shared stage's partials in the epilogue and
+// write `out` directly (dead slots write zeros); otherwise write the unshared partial.
+template <int KVT, int E, int G, bool FUSE>
 __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -77,7 +82,17 @@ __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
   const int step = a.step;
 
   const int par = a.parent_idx[(size_t)step * sumW + slot];
-  if (par < 0) return;                   // dead slot: the merge writes zeros
+  if (par < 0) {                         // dead slot: zero output
+    if constexpr (FUSE) {
+#pragma unroll
+      for (int jj = 0; jj < G; ++jj) {
+        float* dst = a.out + ((size_t)slot * Hq + hk * G + jj) * D + d0;
+#pragma unroll
+        for (int i = 0; i < E; ++i) dst[i] = 0.0f;
+      }
+    }
+    return;
+  }
   const ReqDesc rd = a.req[a.slot_req[slot]];
   const int Wr = rd.W, boff = rd.boff;
 
@@ -142,13 +157,59 @@ __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
     if (lane == 0) atomicOr(a.flags, (int)GRW_FLAG_BAD_PARENT);
     return;
   }
+  if constexpr (!FUSE) {
 #pragma unroll
-  for (int jj = 0; jj < G; ++jj) {
-    const float inv = vscale / l[jj];
-    float* dst = a.ou + ((size_t)slot * Hq + hk * G + jj) * D + d0;
+    for (int jj = 0; jj < G; ++jj) {
+      const float inv = vscale / l[jj];
+      float* dst = a.ou + ((size_t)slot * Hq + hk * G + jj) * D + d0;
 #pragma unroll
-    for (int i = 0; i < E; ++i) dst[i] = o[jj][i] * inv;
-    if (lane == hk * LPH) a.lu[(size_t)slot * Hq + hk * G + jj] = (m[jj] + fast_log2(l[jj])) * kLn2;
+      for (int i = 0; i < E; ++i) dst[i] = o[jj][i] * inv;
+      if (lane == hk * LPH) a.lu[(size_t)slot * Hq + hk * G + jj] = (m[jj] + fast_log2(l[jj])) * kLn2;
+    }
+  } else {
+    // online-softmax merge with the shared partials, in log2 units:
+    // weight of a partial = 2^(lse2_i - M), unshared weight = l * 2^(m - M) on the raw sums
+    const int ns = rd.nsplit;
+    const size_t plane = (size_t)sumW * Hq;
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+      const size_t row = (size_t)slot * Hq + hk * G + jj;
+      float M = m[jj] + fast_log2(l[jj]);          // log2 of the unshared partial's mass
+      for (int i = 0; i < ns; ++i) M = fmaxf(M, a.lpart[i * plane + row] * kLog2e);
+      const float wu = fast_exp2(m[jj] - M) * vscale;   // multiplies the raw sum o
+      float wsum = l[jj] * fast_exp2(m[jj] - M);
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = o[jj][e] * wu;
+      for (int i = 0; i < ns; ++i) {
+        const float w = fast_exp2(a.lpart[i * plane + row] * kLog2e - M);
+        wsum += w;
+        const float* src = a.opart + (i * plane + row) * D + d0;
+        if constexpr (E % 4 == 0) {
+#pragma unroll
+          for (int e = 0; e < E; e += 4) {
+            const floatx4 v = *(const floatx4*)(src + e);
+            acc[e] = fmaf(v.x, w, acc[e]);
+            acc[e + 1] = fmaf(v.y, w, acc[e + 1]);
+            acc[e + 2] = fmaf(v.z, w, acc[e + 2]);
+            acc[e + 3] = fmaf(v.w, w, acc[e + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[e] = fmaf(src[e], w, acc[e]);
+        }
+      }
+      const float inv = 1.0f / wsum;
+      float* dst = a.out + row * D + d0;
+      if constexpr (E % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *(floatx4*)(dst + e) = floatx4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[e] = acc[e] * inv;
+      }
+    }
   }
 }
 
@@ -182,37 +243,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   *dst = acc * (1.0f / wsum);
 }
 
-template <int KVT, int E>
+template <int KVT, int E, bool FUSE>
 hipError_t launch_unshared_g(const AttnArgs& a, hipStream_t s, int blocks) {
   switch (a.g) {
-    case 1: attn_unshared_kernel<KVT, E, 1><<<blocks, 256, 0, s>>>(a); break;
-    case 2: attn_unshared_kernel<KVT, E, 2><<<blocks, 256, 0, s>>>(a); break;
-    default: attn_unshared_kernel<KVT, E, 4><<<blocks, 256, 0, s>>>(a); break;
+    case 1: attn_unshared_kernel<KVT, E, 1, FUSE><<<blocks, 256, 0, s>>>(a); break;
+    case 2: attn_unshared_kernel<KVT, E, 2, FUSE><<<blocks, 256, 0, s>>>(a); break;
+    default: attn_unshared_kernel<KVT, E, 4, FUSE><<<blocks, 256, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
-template <int KVT>
+template <int KVT, bool FUSE>
 hipError_t launch_unshared_e(const AttnArgs& a, hipStream_t s, int blocks) {
   switch ((a.Hkv * a.D) / 64) {
-    case 2: return launch_unshared_g<KVT, 2>(a, s, blocks);
-    case 4: return launch_unshared_g<KVT, 4>(a, s, blocks);
-    case 8: return launch_unshared_g<KVT, 8>(a, s, blocks);
-    default: return launch_unshared_g<KVT, 16>(a, s, blocks);
+    case 2: return launch_unshared_g<KVT, 2, FUSE>(a, s, blocks);
+    case 4: return launch_unshared_g<KVT, 4, FUSE>(a, s, blocks);
+    case 8: return launch_unshared_g<KVT, 8, FUSE>(a, s, blocks);
+    default: return launch_unshared_g<KVT, 16, FUSE>(a, s, blocks);
+  }
+}
+
+template <bool FUSE>
+hipError_t launch_unshared_t(const AttnArgs& a, hipStream_t s) {
+  const int blocks = (a.sumW + 3) / 4;
+  if (blocks == 0) return hipSuccess;
+  switch (a.kv_dtype) {
+    case GRW_F32: return launch_unshared_e<GRW_F32, FUSE>(a, s, blocks);
+    case GRW_BF16: return launch_unshared_e<GRW_BF16, FUSE>(a, s, blocks);
+    default: return launch_unshared_e<GRW_FP8_E4M3, FUSE>(a, s, blocks);
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s) {
-  const int blocks = (a.sumW + 3) / 4;
-  if (blocks == 0) return hipSuccess;
-  switch (a.kv_dtype) {
-    case GRW_F32: return launch_unshared_e<GRW_F32>(a, s, blocks);
-    case GRW_BF16: return launch_unshared_e<GRW_BF16>(a, s, blocks);
-    default: return launch_unshared_e<GRW_FP8_E4M3>(a, s, blocks);
-  }
-}
+hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s) { return launch_unshared_t<false>(a, s); }
+
+hipError_t launch_attn_unshared_merge(const AttnArgs& a, hipStream_t s) { return launch_unshared_t<true>(a, s); }
 
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.sumW * a.Hq * (a.D / 4);

@@ -88,6 +88,7 @@ hipError_t launch_attn_shared_valu(const AttnArgs& a, const ShWork* work, int n_
                                    hipStream_t s);
 hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_unshared_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_select_topk(const SelArgs& a, hipStream_t s);
 hipError_t launch_select_global(const SelArgs& a, hipStream_t s);
 hipError_t launch_beams_init(const ReqDesc* req, const int32_t* slot_req, int32_t sumW,

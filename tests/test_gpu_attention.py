@@ -118,3 +118,31 @@ def test_bf16_generic_head_dim_path(lib):
     layer = attention_layer(wl, 0)
     par = random_parents(wl)
     run_attention(lib, wl, layer, par, W, K, P, [0, 1], all_slots(W))
+
+
+def test_stage_by_stage_equals_fused_path(lib):
+    """Shared, unshared and merge launched one stage at a time (merge as its own kernel over
+    workspace partials) give the same output as the default path (merge fused into the
+    unshared epilogue), and both match the oracle."""
+    wl = workload("qwen06b")
+    W, K, P = request_shapes(wl)
+    layer = attention_layer(wl, 0)
+    par = random_parents(wl, dead_frac=0.1)
+    ws = make_ws(lib, W, K, P, C=16, S=wl.S)
+    dev = upload_layer(layer, wl.q_dtype, wl.kv_dtype)
+    parents = torch.from_numpy(par).cuda()
+    out_a = torch.full((int(W.sum()), wl.Hq, wl.D), float("nan"), device="cuda")
+    out_b = torch.full_like(out_a, float("nan"))
+    d = 2
+    args = (dev["q"][d], dev["k_s"], dev["v_s"], None, None, dev["k_u"], dev["v_u"], parents, d)
+    lib.beam_attn_decode(ws, *args, out_a)
+    for mask in (lib.STAGE_SHARED, lib.STAGE_UNSHARED, lib.STAGE_MERGE):
+        lib.beam_attn_decode_stages(ws, *args, out_b, mask)
+    torch.cuda.synchronize()
+    a, b = out_a.cpu().numpy(), out_b.cpu().numpy()
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    assert np.max(np.abs(a - b)) <= 1e-5
+    attention_vs_oracle(b, layer, par, d, list(W), wl.q_dtype, wl.kv_dtype,
+                        {0: range(int(W[0])), 7: range(int(W[7]))}, TOL["bf16"], label="stagewise")
+    with pytest.raises(lib.GrwError):
+        lib.beam_attn_decode_stages(ws, *args, out_b, 0)
