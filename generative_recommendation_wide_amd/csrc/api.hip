@@ -44,6 +44,7 @@ struct grw_ws {
   int sumW = 0;
   int maxW = 0, maxK = 0;
   int n_work = 0;
+  int n_wide = 0;                // leading items of the work list that use the 8-wave kernel
   std::vector<ReqDesc> req;
 };
 
@@ -85,52 +86,67 @@ void free_all(grw_ws* w) {
   if (w->h_stage) (void)hipHostFree(w->h_stage);
 }
 
-// Shared-stage work list of the MFMA kernel.  Items of one (request, kv head, split)
-// share the same prompt tiles; they are assigned to one XCD (workgroup i runs on XCD
-// i % 8) so the repeated tile reads are served by that XCD's L2.
-void build_mfma_work(grw_ws* w, std::vector<ShWork>& out) {
+// Shared-stage work lists of the MFMA kernels.  Requests with bf16 KV and more than 128
+// query rows per kv head go to the 8-wave kernel (256 rows per item); the others to the
+// 4-wave kernel (128 rows).  Items of one (request, kv head, split) share the same prompt
+// tiles; they are assigned to one XCD (workgroup i runs on XCD i % 8) so the repeated tile
+// reads are served by that XCD's L2.  The wide list comes first, then the narrow one.
+void build_mfma_work(grw_ws* w, std::vector<ShWork>& out, int& n_wide) {
   const grw_limits& L = w->lim;
   const int g = L.Hq / L.Hkv;
-  // balance: aim for >= 2 workgroups per CU, splitting long prompts
-  int64_t total_tiles = 0;
-  for (const ReqDesc& r : w->req)
-    total_tiles += (int64_t)L.Hkv * ceil_div((int64_t)r.W * g, kShRows) * ceil_div(r.P, kShKeys);
-  const int64_t target_items = 2LL * w->n_cu;
-  const int64_t tiles_per_item = std::max<int64_t>(4, ceil_div(total_tiles, target_items));
-  struct Group { int r, h, split, p0, p1, n_items; int64_t tiles; };
-  std::vector<Group> groups;
+  auto is_wide = [&](const ReqDesc& r) {
+    return L.kv_dtype == GRW_BF16 && (int64_t)r.W * g > kShRows;
+  };
+  // balance: aim for about two 4-wave workgroups' worth of work per CU (a wide item counts
+  // twice), splitting long prompts
+  int64_t total_units = 0;
+  for (const ReqDesc& r : w->req) {
+    const int rows = is_wide(r) ? kShRowsWide : kShRows;
+    total_units += (int64_t)L.Hkv * ceil_div((int64_t)r.W * g, rows) * (rows / kShRows) * ceil_div(r.P, kShKeys);
+  }
+  const int64_t target_units = 2LL * w->n_cu;
+  const int64_t tiles_per_item = std::max<int64_t>(4, ceil_div(total_units, target_units));
+  struct Group { int r, h, split, p0, p1, n_items, rows; int64_t tiles; };
+  std::vector<Group> groups[2];
   for (int ri = 0; ri < w->R; ++ri) {
     ReqDesc& r = w->req[ri];
+    const bool wide = is_wide(r);
+    const int rows = wide ? kShRowsWide : kShRows;
     const int64_t ptiles = ceil_div(r.P, kShKeys);
     int ns = (int)std::min<int64_t>(L.max_splits, std::max<int64_t>(1, ceil_div(ptiles, tiles_per_item)));
     const int64_t chunk_tiles = ceil_div(ptiles, ns);
     ns = (int)ceil_div(ptiles, chunk_tiles);
     r.nsplit = ns;
-    const int mt = (int)ceil_div((int64_t)r.W * g, kShRows);
+    const int mt = (int)ceil_div((int64_t)r.W * g, rows);
     for (int s = 0; s < ns; ++s) {
       const int p0 = (int)(s * chunk_tiles * kShKeys);
       const int p1 = (int)std::min<int64_t>(r.P, (s + 1) * chunk_tiles * kShKeys);
       for (int h = 0; h < L.Hkv; ++h)
-        groups.push_back({ri, h, s, p0, p1, mt, (int64_t)mt * ceil_div(p1 - p0, kShKeys)});
+        groups[wide ? 0 : 1].push_back({ri, h, s, p0, p1, mt, rows, (int64_t)mt * ceil_div(p1 - p0, kShKeys)});
     }
   }
-  std::stable_sort(groups.begin(), groups.end(),
-                   [](const Group& a, const Group& b) { return a.tiles > b.tiles; });
-  constexpr int NX = 8;
-  std::vector<std::vector<ShWork>> q(NX);
-  std::vector<int64_t> load(NX, 0);
-  for (const Group& gr : groups) {
-    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    load[x] += gr.tiles;
-    for (int m = 0; m < gr.n_items; ++m)
-      q[x].push_back({gr.r, gr.h, m * kShRows, gr.split, gr.p0, gr.p1, 0, 0});
-  }
-  size_t len = 0;
-  for (auto& v : q) len = std::max(len, v.size());
   out.clear();
-  for (size_t j = 0; j < len; ++j)
-    for (int x = 0; x < NX; ++x)
-      out.push_back(j < q[x].size() ? q[x][j] : ShWork{-1, 0, 0, 0, 0, 0, 0, 0});
+  n_wide = 0;
+  for (int kind = 0; kind < 2; ++kind) {
+    std::vector<Group>& gs = groups[kind];
+    std::stable_sort(gs.begin(), gs.end(), [](const Group& a, const Group& b) { return a.tiles > b.tiles; });
+    constexpr int NX = 8;
+    std::vector<std::vector<ShWork>> q(NX);
+    std::vector<int64_t> load(NX, 0);
+    for (const Group& gr : gs) {
+      const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+      load[x] += gr.tiles;
+      for (int m = 0; m < gr.n_items; ++m)
+        q[x].push_back({gr.r, gr.h, m * gr.rows, gr.split, gr.p0, gr.p1, 0, 0});
+    }
+    size_t len = 0;
+    for (auto& v : q) len = std::max(len, v.size());
+    const size_t before = out.size();
+    for (size_t j = 0; j < len; ++j)
+      for (int x = 0; x < NX; ++x)
+        out.push_back(j < q[x].size() ? q[x][j] : ShWork{-1, 0, 0, 0, 0, 0, 0, 0});
+    if (kind == 0) n_wide = (int)(out.size() - before);
+  }
 }
 
 // Work list of the generic VALU shared stage: one item per (slot, query head, split).
@@ -280,7 +296,8 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   w->R = n_requests;
   w->sumW = (int)sumW;
   std::vector<ShWork> work;
-  if (w->mfma) build_mfma_work(w, work);
+  int n_wide = 0;
+  if (w->mfma) build_mfma_work(w, work, n_wide);
   else build_valu_work(w, work);
   if ((int64_t)work.size() > w->work_cap) return GRW_EUNSUPPORTED;
   // one upload: descriptors, slot -> request map, work list
@@ -303,6 +320,7 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
     return GRW_EDEVICE;
   }
   w->n_work = (int)work.size();
+  w->n_wide = n_wide;
   w->maxW = maxW;
   w->maxK = maxK;
   w->bound = true;
@@ -364,9 +382,14 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
   a.kv_dtype = L.kv_dtype;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (stages & GRW_STAGE_SHARED)
-    e = w->mfma ? launch_attn_shared_mfma(a, w->d_work, w->n_work, s)
-                : launch_attn_shared_valu(a, w->d_work, w->n_work, s);
+  if (stages & GRW_STAGE_SHARED) {
+    if (w->mfma) {
+      e = launch_attn_shared_lds(a, w->d_work, w->n_wide, s);
+      if (e == hipSuccess) e = launch_attn_shared_mfma(a, w->d_work + w->n_wide, w->n_work - w->n_wide, s);
+    } else {
+      e = launch_attn_shared_valu(a, w->d_work, w->n_work, s);
+    }
+  }
   const int um = stages & (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE);
   if (e == hipSuccess && um == (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE)) {
     e = launch_attn_unshared_merge(a, s);        // merge fused into the unshared epilogue

@@ -310,6 +310,203 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
 }
 
 // ---------------------------------------------------------------------------------------
+// Wide-request bf16 path: 8 waves x 32 rows = 256 query rows per workgroup (one request's
+// 128 beams x 2 grouped heads), so each prompt tile read from L2 feeds twice the rows of the
+// 4-wave kernel above.  Tiles move global -> LDS with global_load_lds_dwordx4 (no register
+// staging, no LDS store instructions) into a two-stage ring.  Tiles are unpadded and
+// XOR-swizzled so the MFMA operand reads are conflict-free 16-byte reads:
+//   K tile   [64 keys][128 d]: 16-byte chunk lc of row r sits at chunk lc ^ (r % 16);
+//            row r holds key k_row_key(r), a permutation inside each 32-key block chosen so
+//            that the eight P values a lane feeds one PV k-step are eight consecutive keys;
+//   V^T tile [128 d][64 keys]: chunk lc of row d sits at chunk lc ^ ((d / 2) % 8).
+// Each phase reads all its fragments before its MFMAs so one wait covers the LDS latency.
+// ---------------------------------------------------------------------------------------
+namespace lds {
+
+constexpr int NWAVES = 8;
+constexpr int NSTAGE = 2;
+constexpr int K_BYTES = NT * DH * 2;       // 16 KB
+constexpr int STAGE_BYTES = 2 * K_BYTES;   // K + V^T
+constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int k_row_key(int r) {
+  const int x = r & 31;
+  const int i = x >> 3, hh = (x >> 2) & 1, j = x & 3;
+  return (r & 32) + (i >> 1) * 16 + hh * 8 + (i & 1) * 4 + j;
+}
+
+// Direct-to-LDS loads of the tile at prompt position p: each wave moves 2 KB of K and 2 KB
+// of V^T (lane l of an instruction fills LDS chunk base + l).
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* kb, const uint8_t* vb, int p, int Pp,
+                                           int wave, int lane) {
+  constexpr int PER = 16 / NWAVES;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = wave * PER + i;
+    const int j = blk * 64 + lane;
+    {
+      const int r = j >> 4, lc = (j & 15) ^ (r & 15);
+      const uint8_t* src = kb + ((size_t)(p + k_row_key(r)) * DH + lc * 8) * 2;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + blk * 1024), 16, 0, 0);
+    }
+    {
+      const int d = j >> 3, lc = (j & 7) ^ ((d >> 1) & 7);
+      const uint8_t* src = vb + ((size_t)d * Pp + p + lc * 8) * 2;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + K_BYTES + blk * 1024), 16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_all_vm() {
+  __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | 0);   // vmcnt(0)
+}
+
+__global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_lds_kernel(AttnArgs a, const ShWork* __restrict__ work) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const ShWork wk = work[blockIdx.x];
+  if (wk.r < 0) return;
+  const ReqDesc rd = a.req[wk.r];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = a.g, Hq = a.Hq, h = wk.h;
+  const int nrows = rd.W * g;
+  const int mrow = wk.m0 + wave * 32 + l32;
+  const bool row_ok = mrow < nrows;
+  const int b = row_ok ? mrow / g : 0;
+  const int qh = h * g + (row_ok ? mrow - b * g : 0);
+  const int slot = rd.boff + b;
+  const uint8_t* kb = (const uint8_t*)a.k_shared + (rd.kv_off + (size_t)h * rd.Pp * DH) * 2;
+  const uint8_t* vb = (const uint8_t*)a.v_shared + (rd.kv_off + (size_t)h * DH * rd.Pp) * 2;
+  const int p0 = wk.p0, p1 = wk.p1;
+  const int ntiles = (p1 - p0 + NT - 1) / NT;
+
+  issue_tile(smem, kb, vb, p0, rd.Pp, wave, lane);
+  bf16x8 qf[DH / 16];
+  {
+    const __bf16* qrow = (const __bf16*)a.q + ((size_t)slot * Hq + qh) * DH;
+#pragma unroll
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      if (row_ok) {
+        qf[ks] = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
+      }
+    }
+  }
+  const float c = rsqrtf((float)DH) * kLog2e;
+  float m_run = -INFINITY, l_run = 0.0f;
+  floatx16 o[DH / 32];
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) o[db] = floatx16{};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_all_vm();            // this wave's loads of tile t are in LDS
+    __syncthreads();          // ... and every other wave's; the other stage is free again
+    if (t + 1 < ntiles) issue_tile(smem + ((t + 1) & 1) * STAGE_BYTES, kb, vb, p0 + (t + 1) * NT, rd.Pp, wave, lane);
+    const uint8_t* st = smem + (t & 1) * STAGE_BYTES;
+    const int p = p0 + t * NT;
+
+    floatx16 s0 = floatx16{}, s1 = floatx16{};
+    {
+      bf16x8 kf[2][DH / 16];
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        const int lc = 2 * ks + hi;
+        kf[0][ks] = *(const bf16x8*)(st + l32 * 256 + ((lc ^ (l32 & 15)) << 4));
+        kf[1][ks] = *(const bf16x8*)(st + (32 + l32) * 256 + ((lc ^ (l32 & 15)) << 4));
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][ks], qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][ks], qf[ks], s1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // all K fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 score MFMAs
+      __builtin_amdgcn_s_setprio(0);
+    }
+    // value k of block kb is key p + kb*32 + (k/8)*16 + hi*8 + ((k/4)%2)*4 + k%4
+    if (p + NT > p1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int key = p + ((k >> 3) << 4) + hi * 8 + (((k >> 2) & 1) << 2) + (k & 3);
+        if (key >= p1) s0[k] = -INFINITY;
+        if (key + 32 >= p1) s1[k] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s0[k], s1[k]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    if (__any(mx > m_run + kRescale)) {   // lazy rescale (see the 4-wave kernel)
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    // V^T fragments of all four k-steps, read before the exponentials so their latency hides
+    const uint8_t* vt = st + K_BYTES;
+    bf16x8 vf[4][DH / 32];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int lc = 2 * ks + hi;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        const int d = db * 32 + l32;
+        vf[ks][db] = *(const bf16x8*)(vt + d * 128 + ((lc ^ ((d >> 1) & 7)) << 4));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      s0[k] = fast_exp2(fmaf(s0[k], c, -m_run));
+      s1[k] = fast_exp2(fmaf(s1[k], c, -m_run));
+    }
+    bf16x8 pb[4];
+    pb[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+    pb[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+    pb[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+    pb[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 0, 1), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 2, 3), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 4, 5), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 6, 7), ones, l_run, false);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][db], pb[ks], o[db], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = 1.0f / l;
+  float* dst = a.opart + (((size_t)wk.split * a.sumW + slot) * Hq + qh) * DH;
+#pragma unroll
+  for (int db = 0; db < DH / 32; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
+                   o[db][i * 4 + 3] * inv};
+      *(floatx4*)(dst + db * 32 + i * 8 + hi * 4) = v;
+    }
+  }
+  if (hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
+}
+
+}  // namespace lds
+
+// ---------------------------------------------------------------------------------------
 // Generic VALU shared stage: one workgroup per (slot, query head, split), any dtype and
 // head dim <= 256.  Used for float32 inputs and shapes the MFMA kernel does not cover.
 // Work item fields: r, h = query head, m0 = request-local slot, split, p0, p1.
@@ -389,6 +586,19 @@ hipError_t launch_attn_shared_mfma(const AttnArgs& a, const ShWork* work, int n_
     attn_shared_mfma_kernel<true><<<n_work, 256, 0, s>>>(a, work);
   else
     attn_shared_mfma_kernel<false><<<n_work, 256, 0, s>>>(a, work);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_shared_lds(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  static bool attr_set = false;   // the ring needs more than the default 64 KB of LDS
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lds::attn_shared_lds_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds::SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  lds::attn_shared_lds_kernel<<<n_work, lds::NWAVES * 64, lds::SMEM_BYTES, s>>>(a, work);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct ShWork {
 
 // tile sizes of the MFMA shared-stage kernel
 constexpr int kShRows = 128;   // query rows per workgroup (4 waves x 32 rows)
+constexpr int kShRowsWide = 256;   // query rows per workgroup of the 8-wave bf16 kernel
 constexpr int kShKeys = 64;    // prompt keys per LDS tile
 constexpr int kPadP = 64;      // prompt storage padding
 constexpr int kValuRows = 1;   // the generic VALU shared stage handles one (slot, head) row
@@ -86,6 +87,7 @@ hipError_t launch_attn_shared_mfma(const AttnArgs& a, const ShWork* work, int n_
                                    hipStream_t s);
 hipError_t launch_attn_shared_valu(const AttnArgs& a, const ShWork* work, int n_work,
                                    hipStream_t s);
+hipError_t launch_attn_shared_lds(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s);
 hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_unshared_merge(const AttnArgs& a, hipStream_t s);
