@@ -185,6 +185,76 @@ def stage_timings(wl, st, reps):
     return res
 
 
+def select_roofline(seed, dev, reps):
+    """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
+    262144-entry pools): device time of one call with every beam live (the third decode step,
+    beams from two real selections), against the HBM time of its algorithmic bytes: every
+    beam's log-probability row, the beam scores, and the four output arrays."""
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    from synth import request_shapes, workload
+    wl = workload("wide512u")
+    W, K, P = request_shapes(wl, seed)
+    sumW, C = int(W.sum()), wl.C
+    g = torch.Generator(device=dev).manual_seed(seed + 1)
+    lps = []
+    for _ in range(3):
+        x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
+        lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
+        del x
+    ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
+                       max_C=C, max_S=wl.S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                       q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
+    ws.bind_batch(W, K, P)
+    loop = grw.DecodeLoop(ws, wl.S, C, None, device=dev)
+    ws.beams_init(loop.scores[0], loop.nodes[0])
+    loop.select_step(0, lps[0])
+    loop.select_step(1, lps[1])
+    sc, nd = loop.scores[0].clone(), loop.nodes[0].clone()     # step-2 input beams
+    live = int((sc > float("-inf")).sum())
+    tok, par = torch.empty(sumW, dtype=torch.int32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
+    osc, ond = torch.empty(sumW, dtype=torch.float32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    Wm, Km = int(W.max()), int(K.max())
+
+    def fn():
+        grw.beam_select(ws, lps[2], sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+    ms_eager = time_stage(fn, reps, stream)
+    ref = (tok.clone(), par.clone(), osc.clone())
+    tok.fill_(-7)
+    # device time without host launch overhead: replay a captured graph of `reps` calls
+    # (the select kernels record no memset nodes)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(3):
+        graph.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (3 * reps)
+    del graph
+    same = bool(torch.equal(tok, ref[0]) and torch.equal(par, ref[1]) and
+                torch.equal(osc.view(torch.int32), ref[2].view(torch.int32)))
+    pools = [ws.pool_size(r) for r in range(len(W))]
+    bytes_ = sumW * C * 4.0 + sumW * 4.0 + sumW * 16.0
+    t = ms / 1e3
+    achieved = bytes_ / t / 1e9
+    ws.close()
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "workload": "wide512u",
+            "live_beams": live, "bytes_per_call": bytes_, "avg_call_us": round(t * 1e6, 2),
+            "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
+            "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
+            "kernels": "select_pilot_kernel + select_fused_kernel"}
+
+
 # ----------------------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample of the same workload
 # ----------------------------------------------------------------------------------------
@@ -356,6 +426,8 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=3)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
+    ap.add_argument("--select-only", action="store_true",
+                    help="only the beam_select measurement on the unconstrained wide pool (for kernel traces)")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -380,6 +452,9 @@ def main():
     wl = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.select_only:
+        print(json.dumps(select_roofline(args.seed, dev, 20)), flush=True)
+        return 0
     log(f"[bench] setting up {wl.name} ...")
     t_setup = time.perf_counter()
     st = setup(wl, args.seed, dev)
@@ -419,6 +494,10 @@ def main():
                 "kernel": DOMINANT, "flops_per_launch": flops, "avg_launch_us": round(t_shared * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_,
                 "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1)}
+    sel_roof = None
+    if args.stage_reps > 0:
+        sel_roof = select_roofline(args.seed, dev, 20 * args.stage_reps)
+        log(f"[bench] select on wide512u: {sel_roof}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -453,6 +532,7 @@ def main():
                    "device_flags": flags},
         "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
+        "select_roofline": sel_roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

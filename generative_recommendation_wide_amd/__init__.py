@@ -77,6 +77,12 @@ class Workspace:
         _lib.check("grw_ws_splits", _L.grw_ws_splits(self.handle, r, ctypes.byref(v)))
         return v.value
 
+    def pool_size(self, r: int, stream=None) -> int:
+        """Candidate-pool entries of request r kept by the last beam_select (synchronises)."""
+        v = ctypes.c_int64()
+        _lib.check("grw_ws_pool_size", _L.grw_ws_pool_size(self.handle, r, _stream(stream), ctypes.byref(v)))
+        return v.value
+
     def error_flags(self, stream=None) -> int:
         v = ctypes.c_int32()
         _lib.check("grw_ws_error", _L.grw_ws_error(self.handle, _stream(stream), ctypes.byref(v)))

@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(HERE, "libgrw.so")
 GRW_OK, GRW_EINVAL, GRW_ENOMEM, GRW_EDEVICE, GRW_EUNSUPPORTED, GRW_ESTATE = range(6)
 GRW_F32, GRW_BF16, GRW_FP8_E4M3 = 0, 1, 2
 FLAG_NAN_LOGPROB, FLAG_POS_LOGPROB, FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING = 1, 2, 4, 8, 16
+FLAG_POOL_CORRUPT = 32
 STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
             "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
-            "grw_status_str"]
+            "grw_ws_pool_size", "grw_status_str"]
 
 
 class GrwLimits(ctypes.Structure):
@@ -58,6 +59,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "grw_backtrack": [vp, i32p, i32p, i32, i32p, vp],
         "grw_ws_error": [vp, vp, ctypes.POINTER(i32)],
         "grw_ws_splits": [vp, i32, ctypes.POINTER(i32)],
+        "grw_ws_pool_size": [vp, i32, vp, ctypes.POINTER(ctypes.c_int64)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

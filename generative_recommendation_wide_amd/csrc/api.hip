@@ -32,8 +32,12 @@ struct grw_ws {
   float* d_lu = nullptr;
   uint64_t* d_pool = nullptr;
   int64_t pool_cap = 0;
-  uint32_t* d_pool_count = nullptr;
+  int32_t* d_surv_count = nullptr;
   uint32_t* d_bound = nullptr;
+  int32_t* d_pilot_desc = nullptr;
+  uint64_t* d_pilot_buf = nullptr;
+  int32_t* d_order = nullptr;
+  uint32_t* d_step_state = nullptr;    // [3][max_requests]: pilot count, pilot ready, done count
   int32_t* d_flags = nullptr;
   // pinned host staging for the bind upload
   void* h_stage = nullptr;
@@ -45,6 +49,7 @@ struct grw_ws {
   int maxW = 0, maxK = 0;
   int n_work = 0;
   int n_wide = 0;                // leading items of the work list that use the 8-wave kernel
+  int n_pilots = 0;              // pilot workgroups of the selection
   std::vector<ReqDesc> req;
 };
 
@@ -80,8 +85,12 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_ou);
   (void)hipFree(w->d_lu);
   (void)hipFree(w->d_pool);
-  (void)hipFree(w->d_pool_count);
+  (void)hipFree(w->d_surv_count);
   (void)hipFree(w->d_bound);
+  (void)hipFree(w->d_pilot_desc);
+  (void)hipFree(w->d_order);
+  (void)hipFree(w->d_step_state);
+  (void)hipFree(w->d_pilot_buf);
   (void)hipFree(w->d_flags);
   if (w->h_stage) (void)hipHostFree(w->h_stage);
 }
@@ -147,6 +156,21 @@ void build_mfma_work(grw_ws* w, std::vector<ShWork>& out, int& n_wide) {
         out.push_back(j < q[x].size() ? q[x][j] : ShWork{-1, 0, 0, 0, 0, 0, 0, 0});
     if (kind == 0) n_wide = (int)(out.size() - before);
   }
+}
+
+// Pilot beams of the selection: each pilot contributes one candidate per group of
+// pilot_g threads (a power of two; 256 / pilot_g <= top_k, so the contributions of one beam
+// never outnumber its pool entries).  Enough pilots for about 8 W candidates, at most
+// kMaxPilots beams and kPilotCap candidates per request.
+void set_pilots(ReqDesc& d, int32_t& pilot_off) {
+  int per = 1;
+  while (per * 2 <= std::min(d.K, 256)) per *= 2;
+  d.pilot_g = 256 / per;
+  const int64_t want = ceil_div(8LL * d.W, per);
+  int J = (int)std::min<int64_t>({(int64_t)d.W, (int64_t)kMaxPilots, (int64_t)(kPilotCap / per), want});
+  d.n_pilot = std::max(1, J);
+  d.pilot_off = pilot_off;
+  pilot_off += kPilotCap;
 }
 
 // Work list of the generic VALU shared stage: one item per (slot, query head, split).
@@ -229,19 +253,25 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_ou, B * L.Hq * L.D);
   if (st == GRW_OK) st = dev_alloc(&w->d_lu, B * L.Hq);
   if (st == GRW_OK) st = dev_alloc(&w->d_pool, w->pool_cap);
-  if (st == GRW_OK) st = dev_alloc(&w->d_pool_count, L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_surv_count, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 4 * B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_order, B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_step_state, 3LL * L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
   if (st == GRW_OK) {
-    w->stage_bytes = sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * B + sizeof(ShWork) * items;
+    w->stage_bytes = sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * B + sizeof(ShWork) * items +
+                     sizeof(int32_t) * 5 * B;
     if (hipHostMalloc(&w->h_stage, w->stage_bytes, hipHostMallocDefault) != hipSuccess) {
       w->h_stage = nullptr;
       st = GRW_ENOMEM;
     }
   }
   if (st == GRW_OK) {
-    if (hipMemset(w->d_pool_count, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
-        hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
+    if (hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
+        hipMemset(w->d_step_state, 0, sizeof(uint32_t) * 3 * L.max_requests) != hipSuccess ||
+
         hipMemset(w->d_flags, 0, sizeof(int32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
       st = GRW_EDEVICE;
@@ -271,6 +301,7 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   std::vector<ReqDesc> req(n_requests);
   int64_t sumW = 0, kv = 0, pool = 0;
   int maxW = 0, maxK = 0;
+  int32_t pilot_off = 0;
   for (int r = 0; r < n_requests; ++r) {
     const int W = W_host[r], K = K_host[r], P = P_host[r];
     if (W < 1 || W > L.max_W || K < 1 || K > L.max_K || P < 1 || P > L.max_P) return GRW_EINVAL;
@@ -281,6 +312,7 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
     d.nsplit = 1;
     d.kv_off = kv * L.Hkv * L.D;
     d.pool_off = pool;
+    set_pilots(d, pilot_off);
     sumW += W;
     kv += d.Pp;
     pool += (int64_t)W * K;
@@ -305,15 +337,37 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   ReqDesc* hreq = (ReqDesc*)h;
   int32_t* hslot = (int32_t*)(h + sizeof(ReqDesc) * L.max_requests);
   ShWork* hwork = (ShWork*)(h + sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * L.max_total_beams);
+  int32_t* hpilot = (int32_t*)(hwork + w->work_cap);
   std::memcpy(hreq, w->req.data(), sizeof(ReqDesc) * n_requests);
-  for (int r = 0; r < n_requests; ++r)
+  int32_t* horder = hpilot + 4 * L.max_total_beams;
+  int n_pilots = 0;
+  for (int r = 0; r < n_requests; ++r) {
     for (int b = 0; b < req[r].W; ++b) hslot[req[r].boff + b] = r;
+    const int per = 256 / req[r].pilot_g;
+    for (int j = 0; j < req[r].n_pilot; ++j, ++n_pilots) {
+      hpilot[4 * n_pilots + 0] = req[r].boff + j;
+      hpilot[4 * n_pilots + 1] = r;
+      hpilot[4 * n_pilots + 2] = req[r].pilot_off + j * per;
+      hpilot[4 * n_pilots + 3] = req[r].pilot_g;
+    }
+  }
+  // fused-step workgroup order: every request's pilot slots, then the remaining slots
+  for (int p = 0; p < n_pilots; ++p) horder[p] = hpilot[4 * p];
+  {
+    int o = n_pilots;
+    for (int r = 0; r < n_requests; ++r)
+      for (int b = req[r].n_pilot; b < req[r].W; ++b) horder[o++] = req[r].boff + b;
+  }
   std::memcpy(hwork, work.data(), sizeof(ShWork) * work.size());
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(w->d_req, hreq, sizeof(ReqDesc) * n_requests, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(w->d_slot_req, hslot, sizeof(int32_t) * sumW, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !work.empty())
     e = hipMemcpyAsync(w->d_work, hwork, sizeof(ShWork) * work.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(w->d_pilot_desc, hpilot, sizeof(int32_t) * 4 * n_pilots, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(w->d_order, horder, sizeof(int32_t) * sumW, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     w->bound = false;
@@ -321,6 +375,7 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   }
   w->n_work = (int)work.size();
   w->n_wide = n_wide;
+  w->n_pilots = n_pilots;
   w->maxW = maxW;
   w->maxK = maxK;
   w->bound = true;
@@ -429,16 +484,28 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
   a.sumW = w->sumW;
   a.R = w->R;
   a.pool = w->d_pool;
-  a.pool_count = w->d_pool_count;
+  a.surv_count = w->d_surv_count;
   a.bound = w->d_bound;
+  a.pilot_desc = w->d_pilot_desc;
+  a.n_pilots = w->n_pilots;
+  a.pilot_buf = w->d_pilot_buf;
+  a.order = w->d_order;
+  a.pilot_count = w->d_step_state;
+  a.pilot_ready = w->d_step_state + L.max_requests;
+  a.done_count = w->d_step_state + 2 * L.max_requests;
   a.out_token = out_token;
   a.out_parent = out_parent;
   a.out_score = out_score;
   a.out_node = out_node;
   a.flags = w->d_flags;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_select_topk(a, s);
-  if (e == hipSuccess) e = launch_select_global(a, s);
+  hipError_t e;
+  if (select_fused_ok(C, w->maxW)) {
+    e = launch_select_fused(a, s);
+  } else {
+    e = launch_select_topk(a, s);
+    if (e == hipSuccess) e = launch_select_global(a, s);
+  }
   return hip_status(e);
 }
 
@@ -460,6 +527,21 @@ int grw_ws_error(grw_ws* w, void* stream, int32_t* flags) {
   if (e == hipSuccess) e = hipMemset(w->d_flags, 0, sizeof(int32_t));
   if (e == hipSuccess) e = hipDeviceSynchronize();
   *flags = v;
+  return hip_status(e);
+}
+
+int grw_ws_pool_size(grw_ws* w, int32_t r, void* stream, int64_t* pool_size) {
+  if (!w || !pool_size) return GRW_EINVAL;
+  if (!w->bound) return GRW_ESTATE;
+  if (r < 0 || r >= w->R) return GRW_EINVAL;
+  const ReqDesc& d = w->req[r];
+  std::vector<int32_t> cnt(d.W);
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(cnt.data(), w->d_surv_count + d.boff, sizeof(int32_t) * d.W, hipMemcpyDeviceToHost);
+  int64_t n = 0;
+  for (int32_t c : cnt) n += c;
+  *pool_size = n;
   return hip_status(e);
 }
 

@@ -16,6 +16,10 @@ struct ReqDesc {
   int32_t nsplit;    // shared-stage partial results of this request
   int64_t kv_off;    // element offset of the request's prompt block in k_shared / v_shared
   int64_t pool_off;  // first candidate-pool entry of the request (W * min(K, C_max) entries)
+  int32_t n_pilot;   // pilot beams of the selection (slots boff .. boff + n_pilot - 1)
+  int32_t pilot_g;   // threads per pilot group (one candidate per group; 256 / pilot_g <= K)
+  int32_t pilot_off; // first pilot-buffer entry of the request
+  int32_t pad_;
 };
 
 // One shared-stage workgroup: query rows [m0, m0 + rows) of kv head h of request r,
@@ -38,6 +42,12 @@ constexpr int kSelCap = 4096;      // LDS candidate buffer of the per-beam top-k
 constexpr int kSelChunk = 1024;    // candidates appended per round (256 threads x 4)
 constexpr int kMaxK = kSelCap - kSelChunk - 1024;   // 2048
 constexpr int kMaxW = 8192;        // final sort capacity of the global select
+constexpr int kRegC = 32;          // candidates per thread of the one-pass per-beam path
+constexpr int kOnePass = 256 * kRegC;   // rows up to this length take the one-pass path
+constexpr int kMaxPilots = 64;     // pilot beams per request
+constexpr int kPilotCap = 4096;    // pilot candidates per request
+constexpr int kHistBins = 4096;    // survivor histogram bins of the global select
+constexpr int kBinCap = 1024;      // largest histogram bin the global select ranks in place
 
 struct AttnArgs {
   const ReqDesc* req;
@@ -72,9 +82,17 @@ struct SelArgs {
   int32_t n_internal;
   int32_t C;
   int32_t sumW, R;
-  uint64_t* pool;
-  uint32_t* pool_count;     // [R]
+  uint64_t* pool;           // per request: W_r regions of K_r entries (one per beam slot)
+  int32_t* surv_count;      // [sumW] entries in each beam's pool region
   uint32_t* bound;          // [R] ordered-key lower bound of the W_r-th best key
+  const int32_t* pilot_desc;   // [n_pilots][4] beam slot, request, first pilot-buffer entry,
+                               // threads per group, of each pilot workgroup
+  int32_t n_pilots;
+  uint64_t* pilot_buf;      // [R][kPilotCap] pilot candidates
+  const int32_t* order;     // [sumW] beam slot of each fused-step workgroup (pilots first)
+  uint32_t* pilot_count;    // [R] pilots finished this step (fused step)
+  uint32_t* pilot_ready;    // [R] 1 once the pilot bound is published (fused step)
+  uint32_t* done_count;     // [R] workgroups finished this step (fused step)
   int32_t* out_token;
   int32_t* out_parent;
   float* out_score;
@@ -93,6 +111,8 @@ hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_unshared_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_select_topk(const SelArgs& a, hipStream_t s);
 hipError_t launch_select_global(const SelArgs& a, hipStream_t s);
+bool select_fused_ok(int C, int max_W);
+hipError_t launch_select_fused(const SelArgs& a, hipStream_t s);
 hipError_t launch_beams_init(const ReqDesc* req, const int32_t* slot_req, int32_t sumW,
                              float* scores, int32_t* nodes, hipStream_t s);
 hipError_t launch_backtrack(const ReqDesc* req, const int32_t* slot_req, int32_t sumW,

@@ -7,20 +7,31 @@
 // Keys are compared as 64-bit composites (order-preserving float key, ~flat index), so one
 // unsigned comparison orders by (key descending, flat index ascending) and every
 // candidate is distinct: the selection is unique and deterministic whatever the order in
-// which workgroups run.
+// which workgroups run.  A composite of a real candidate is never 0, so 0 marks "empty".
 //
-// select_topk: one workgroup per live beam slot.  Candidates are the codes of the beam's
-//   CSR trie row (or all C codes).  They stream through an LDS buffer; whenever it fills,
-//   a radix select keeps the beam's top_k and raises the admission threshold, so a long
-//   row costs one HBM read.  The survivors go to the request's pool (one atomic
-//   reservation per workgroup).  A beam that alone holds >= W_r survivors publishes its
-//   W_r-th best key as a lower bound of the request's W_r-th best; beams whose score is
-//   below that bound exit without reading their row (log-probabilities are <= 0, so no
-//   key exceeds its beam's score), and candidates below it are never buffered.
-// select_global: one workgroup per request: radix select of the W_r-th best pool entry,
-//   gather, bitonic sort in LDS, then the outputs (the exact float32 score is recomputed
-//   from its two operands, the trie child by a binary search of the parent's row).
-//   It leaves the pool counter and the bound at zero for the next step.
+// Kernels per step:
+//
+// select_pilot / select_bound: the first few slots of each request (the best beams of the
+//   previous step) are pilots.  Each pilot contributes one candidate per group of threads,
+//   at most top_k of them; the W_r-th best of a request's contributions is a lower bound of
+//   its W_r-th best pool entry, because a pilot beam's i-th best contribution is at most
+//   its i-th best candidate and its top_k candidates are all in the pool.
+// select_topk: one workgroup per beam slot; each writes its survivors to its own region of
+//   the request's pool (no shared counters).  A beam whose score is below the bound keeps
+//   nothing and reads nothing: log-probabilities are <= 0, so no key exceeds its beam's
+//   score.  Rows of up to 8192 candidates are read once into registers; candidates below
+//   the bound are dropped, and a radix select over the registers keeps the beam's top_k
+//   when more remain.  Longer rows stream through an LDS buffer that a radix select trims
+//   to top_k whenever it fills.  A beam that alone holds >= W_r survivors raises the bound
+//   to its own W_r-th best.
+// select_global: one workgroup per request.  The beams' survivor counts give every entry a
+//   place in one index range.  A histogram of the entries' keys (bins measured down from
+//   the best live score) finds the bin that holds the W_r-th best entry; the entries of
+//   that bin and all better bins are placed bin by bin and ranked inside their bin, which
+//   gives every winner its output position directly.  When a bin is too large to rank in
+//   place, a radix select and a bitonic sort in LDS do the same job.  The outputs carry the
+//   exact float32 score (recomputed from its two operands) and the trie child (binary
+//   search of the parent's row).  The kernel leaves the bound at zero for the next step.
 #include "device_common.h"
 #include "grw_internal.h"
 
@@ -28,12 +39,41 @@ namespace grw {
 
 namespace {
 
-// Threshold T such that exactly N of the n distinct entries get(0..n-1) are >= T
-// (1 <= N <= n): most-significant-digit-first radix select, 8-bit digits, histograms in
-// LDS, stopping as soon as the chosen digit's bucket holds exactly the entries still
-// needed.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Pick, from a 256-bucket histogram, the digit whose bucket holds the `need`-th largest
+// entry (buckets scanned from digit 255 down).  Run by the first wave; writes the digit,
+// the count of entries in higher buckets and the bucket's own count to scr[0..2].
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, uint32_t* scr) {
+  const int lane = threadIdx.x;
+  const uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
+  const uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
+  const uint32_t tot = c0 + c1 + c2 + c3;
+  const uint32_t incl = (uint32_t)wave_inclusive_scan((int)tot);
+  const uint32_t excl = incl - tot;
+  if (excl < need && need <= incl) {
+    uint32_t acc = excl;
+    int dsel;
+    if (acc + c0 >= need) dsel = 255 - 4 * lane;
+    else if ((acc += c0) + c1 >= need) dsel = 254 - 4 * lane;
+    else if ((acc += c1) + c2 >= need) dsel = 253 - 4 * lane;
+    else { acc += c2; dsel = 252 - 4 * lane; }
+    scr[0] = (uint32_t)dsel;
+    scr[1] = acc;
+    scr[2] = hist[dsel];
+  }
+}
+
+// Threshold T such that exactly N of the non-zero entries among get(0..n-1) are >= T
+// (1 <= N <= their count; entries distinct): most-significant-digit-first radix select,
+// 8-bit digits, histograms in LDS, stopping as soon as the chosen digit's bucket holds
+// exactly the entries still needed.
 template <int NT, typename Get>
-__device__ uint64_t block_select_threshold(Get get, int n, int N, uint32_t* hist, uint32_t* scr) {
+__device__ __forceinline__ uint64_t block_select_threshold(Get get, int n, int N, uint32_t* hist, uint32_t* scr) {
   uint64_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)N;
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -41,37 +81,173 @@ __device__ uint64_t block_select_threshold(Get get, int n, int N, uint32_t* hist
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint64_t v = get(i);
-      if ((v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
+      if (v != 0 && (v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
-      const uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
-      const uint32_t tot = c0 + c1 + c2 + c3;
-      const uint32_t incl = (uint32_t)wave_inclusive_scan((int)tot);
-      const uint32_t excl = incl - tot;
-      if (excl < need && need <= incl) {
-        uint32_t acc = excl;
-        int dsel;
-        if (acc + c0 >= need) dsel = 255 - 4 * lane;
-        else if ((acc += c0) + c1 >= need) dsel = 254 - 4 * lane;
-        else if ((acc += c1) + c2 >= need) dsel = 253 - 4 * lane;
-        else { acc += c2; dsel = 252 - 4 * lane; }
-        scr[0] = (uint32_t)dsel;
-        scr[1] = acc;
-        scr[2] = hist[dsel];
-      }
-    }
+    if (threadIdx.x < 64) pick_digit(hist, need, scr);
     __syncthreads();
     const uint32_t dsel = scr[0], above = scr[1], cnt = scr[2];
     __syncthreads();
     need -= above;
     prefix |= (uint64_t)dsel << shift;
     mask |= (uint64_t)255u << shift;
-    if (cnt == need) return prefix;
+    if (cnt == need) return prefix > 0 ? prefix : 1;
   }
   return prefix;
+}
+
+// Block-wide OR and AND of the threads' values (NT threads; red holds 2 NT / 64 entries).
+template <int NT>
+__device__ __forceinline__ void block_or_and(uint64_t& o, uint64_t& an, uint64_t* red) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) {
+    o |= shfl_xor_u64(o, s);
+    an &= shfl_xor_u64(an, s);
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { red[wave] = o; red[NW + wave] = an; }
+  __syncthreads();
+  o = 0;
+  an = ~0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { o |= red[w]; an &= red[NW + w]; }
+}
+
+// Sum over the 256 threads of a workgroup; red holds 4 entries.
+__device__ __forceinline__ int block_sum256(int v, int* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Exclusive prefix of v over the 256 threads; *total receives the sum.  red holds 4 entries.
+__device__ __forceinline__ int block_excl_scan256(int v, int* red, int* total) {
+  const int incl = wave_inclusive_scan(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += red[w];
+  *total = red[0] + red[1] + red[2] + red[3];
+  return before + incl - v;
+}
+
+// Threshold T such that exactly N of the non-zero entries held by the threads are >= T
+// (1 <= N <= their count; NT threads, each holding NR entries get(0..NR-1), 0 = none).
+// Radix select as above, starting at the highest bit in which the entries differ.
+template <int NT, int NR, typename Get>
+__device__ __forceinline__ uint64_t regs_select_threshold(Get get, int N, uint32_t* hist, uint32_t* scr,
+                                                          uint64_t* red) {
+  uint64_t o = 0, an = ~0ull;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const uint64_t x = get(k);
+    if (x) { o |= x; an &= x; }
+  }
+  block_or_and<NT>(o, an, red);
+  const uint64_t diff = o ^ an;
+  if (diff == 0) return o;                         // a single distinct entry
+  const int hb = 63 - __builtin_clzll(diff);
+  const uint64_t below = (hb == 63) ? ~0ull : ((1ull << (hb + 1)) - 1);
+  uint64_t known = ~below;
+  uint64_t prefix = o & known;
+  uint32_t need = (uint32_t)N;
+  int shift = hb >= 7 ? hb - 7 : 0;
+  while (true) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const uint64_t x = get(k);
+      if (x != 0 && (x & known) == prefix) atomicAdd(&hist[(uint32_t)(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) pick_digit(hist, need, scr);
+    __syncthreads();
+    const uint32_t dsel = scr[0], above = scr[1], cnt = scr[2];
+    __syncthreads();
+    need -= above;
+    prefix |= (uint64_t)dsel << shift;
+    known |= (uint64_t)255u << shift;
+    if (cnt == need || shift == 0) return prefix > 0 ? prefix : 1;
+    shift = shift >= 8 ? shift - 8 : 0;
+  }
+}
+
+// 32-bit radix select over the non-zero values held by the threads (NT threads, NR values
+// get(0..NR-1) each, n of them non-zero in total, 1 <= N <= n).  Returns v, need and cnt:
+// exactly N - need values exceed v, and cnt values lie in [v, v + span) where span covers
+// the bits not yet examined; cnt == need means the values >= v are exactly N, otherwise all
+// 32 bits are examined and cnt values equal v, of which `need` are wanted.
+struct Sel32 { uint32_t v, need, cnt; };
+
+template <int NT, int NR, typename Get>
+__device__ __forceinline__ Sel32 regs_select32(Get get, uint32_t N, uint32_t n, uint32_t* hist, uint32_t* scr,
+                                               uint32_t* red) {
+  constexpr int NW = NT / 64;
+  uint32_t o = 0, an = ~0u;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const uint32_t x = get(k);
+    if (x) { o |= x; an &= x; }
+  }
+#pragma unroll
+  for (int sh = 32; sh > 0; sh >>= 1) {
+    o |= __shfl_xor(o, sh, 64);
+    an &= __shfl_xor(an, sh, 64);
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[NW + (threadIdx.x >> 6)] = an; }
+  __syncthreads();
+  o = 0;
+  an = ~0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { o |= red[w]; an &= red[NW + w]; }
+  const uint32_t diff = o ^ an;
+  if (diff == 0) return Sel32{o, N, n};            // all values equal
+  const int hb = 31 - __builtin_clz(diff);
+  const uint32_t below = hb == 31 ? ~0u : ((1u << (hb + 1)) - 1);
+  uint32_t known = ~below;
+  uint32_t prefix = o & known;
+  uint32_t need = N;
+  int shift = hb >= 7 ? hb - 7 : 0;
+  while (true) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const uint32_t x = get(k);
+      if (x != 0 && (x & known) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) pick_digit(hist, need, scr);
+    __syncthreads();
+    const uint32_t dsel = scr[0], above = scr[1], cnt = scr[2];
+    __syncthreads();
+    need -= above;
+    prefix |= dsel << shift;
+    known |= 255u << shift;
+    if (cnt == need || shift == 0) return Sel32{prefix, need, cnt};
+    shift = shift >= 8 ? shift - 8 : 0;
+  }
+}
+
+// Composite threshold T such that exactly N of the candidates held by the threads are
+// >= T, from their ordered keys ok(k) (0 = none) and flat indices flat(k); n candidates in
+// all.  Ties at the threshold key are resolved by a second select on ~flat.
+template <int NT, int NR, typename GetKey, typename GetFlat>
+__device__ __forceinline__ uint64_t regs_select_composite(GetKey ok, GetFlat flat, uint32_t N, uint32_t n,
+                                                          uint32_t* hist, uint32_t* scr, uint32_t* red) {
+  const Sel32 t = regs_select32<NT, NR>(ok, N, n, hist, scr, red);
+  if (t.cnt == t.need) return (uint64_t)t.v << 32;
+  const Sel32 t2 = regs_select32<NT, NR>([&](int k) { return ok(k) == t.v ? ~flat(k) : 0u; }, t.need, t.cnt, hist,
+                                         scr, red);
+  return ((uint64_t)t.v << 32) | t2.v;
 }
 
 // Append each thread's `ne` entries (registers) to dst[*counter ...] (LDS counter).
@@ -91,7 +267,7 @@ __device__ __forceinline__ void block_append(uint64_t* dst, int* counter, const 
 }
 
 // Keep only entries >= T of buf[0..n) (in LDS), compacted to the front; returns the new n.
-__device__ int block_compact_ge(uint64_t* buf, int n, uint64_t T, int* counter) {
+__device__ __forceinline__ int block_compact_ge(uint64_t* buf, int n, uint64_t T, int* counter) {
   constexpr int PER = kSelCap / 256;   // 16 entries per thread
   uint64_t v[PER];
   int nv = 0;
@@ -111,207 +287,806 @@ __device__ int block_compact_ge(uint64_t* buf, int n, uint64_t T, int* counter) 
   return *counter;
 }
 
-__global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
-  __shared__ uint64_t buf[kSelCap];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scr[4];
-  __shared__ int cnt_s;
-  __shared__ int flag_s;
-  __shared__ uint32_t pos_s;
-  const int slot = blockIdx.x;
-  const int tid = threadIdx.x;
-  const float s = a.scores[slot];
-  if (s == -INFINITY) return;
-  if (__builtin_isnan(s)) {
-    if (tid == 0) atomicOr(a.flags, (int)GRW_FLAG_NAN_LOGPROB);
-    return;
-  }
-  const int r = a.slot_req[slot];
-  const ReqDesc rd = a.req[r];
-  const uint32_t s_key = ordered_key(s);
-  // one read of the request's bound, shared by the workgroup so the exit is uniform
-  if (tid == 0) pos_s = __hip_atomic_load(&a.bound[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  uint32_t tau = pos_s;
-  if (s_key < tau) return;                       // early exit: no key of this beam can make it
-
-  int cnt = a.C;
-  const int32_t* codes = nullptr;
+// The candidates of a beam slot: its CSR trie row (or all C codes).  Returns false when
+// the node is out of range.
+__device__ __forceinline__ bool beam_row(const SelArgs& a, int slot, int& cnt, const int32_t*& codes) {
+  cnt = a.C;
+  codes = nullptr;
   if (a.row_ptr != nullptr) {
     const int node = a.nodes[slot];
-    if (node < 0 || node >= a.n_internal) {
-      if (tid == 0) atomicOr(a.flags, (int)GRW_FLAG_BAD_NODE);
-      return;
-    }
+    if (node < 0 || node >= a.n_internal) return false;
     const int beg = a.row_ptr[node];
     cnt = a.row_ptr[node + 1] - beg;
     codes = a.code + beg;
   }
-  const float* lprow = a.logprobs + (size_t)slot * a.C;
-  const uint32_t flat_base = (uint32_t)(slot - rd.boff) * (uint32_t)a.C;
-  const int K = rd.K;
-  if (tid == 0) { cnt_s = 0; flag_s = 0; }
-  __syncthreads();
+  return true;
+}
 
-  int n = 0;
-  int fl = 0;
-  for (int base = 0; base < cnt; base += kSelChunk) {
-    if (n + kSelChunk > kSelCap) {               // buffer full: keep the top K, raise tau
-      const uint64_t T = block_select_threshold<256>([&](int i) { return buf[i]; }, n, K, hist, scr);
-      n = block_compact_ge(buf, n, T, &cnt_s);
-      const uint32_t tk = (uint32_t)(T >> 32);
-      tau = max(tau, tk);
-      tau = max(tau, __hip_atomic_load(&a.bound[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
-    uint64_t e[4];
-    int ne = 0;
+// Composite key of one candidate (0 when it is not a candidate), with the precondition flags.
+__device__ __forceinline__ uint64_t candidate(float s, float lp, uint32_t flat, int& fl) {
+  if (__builtin_isnan(lp)) { fl |= GRW_FLAG_NAN_LOGPROB; return 0; }
+  if (lp > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
+  const float key = s + lp;
+  if (key == -INFINITY) return 0;
+  return composite_key(ordered_key(key), flat);
+}
+
+// Row layouts of the one-read path: kFull — all C codes with C % 4 == 0 and an aligned row,
+// thread t holding codes 4 (t + 256 q) + e so that every load is a full 1 KB wave line;
+// kFullScalar — all C codes, thread t holding codes t + 256 k; kTrie — a CSR trie row,
+// thread t holding row positions t + 256 k (their codes are kept).
+enum RowLayout { kFull = 0, kFullScalar = 1, kTrie = 2 };
+
+template <int L>
+struct RowRegs {
+  float lp[kRegC];
+  int code[L == kTrie ? kRegC : 1];
+  __device__ __forceinline__ int code_of(int k) const {
+    if constexpr (L == kTrie) return code[k];
+    else if constexpr (L == kFull) return 4 * ((int)threadIdx.x + 256 * (k >> 2)) + (k & 3);
+    else return (int)threadIdx.x + 256 * k;
+  }
+  __device__ __forceinline__ bool valid(int k, int cnt) const {
+    if constexpr (L == kTrie) return code[k] >= 0;
+    else return code_of(k) < cnt;
+  }
+};
+
+// Read a row of up to kOnePass candidates into registers (one load per candidate).
+template <int L>
+__device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const float* lprow,
+                                         const int32_t* codes, int cnt, int& fl) {
+  const int tid = threadIdx.x;
+  if constexpr (L == kFull) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = base + tid + 256 * k;
-      if (i < cnt) {
-        const int c = codes ? codes[i] : i;
-        if ((unsigned)c >= (unsigned)a.C) {        // corrupt trie row: never read outside the row
-          fl |= GRW_FLAG_BAD_NODE;
-          continue;
-        }
-        const float lp = lprow[c];
-        if (__builtin_isnan(lp)) {
-          fl |= GRW_FLAG_NAN_LOGPROB;
-        } else {
-          if (lp > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
-          const float key = s + lp;
-          if (key != -INFINITY) {
-            const uint32_t ok = ordered_key(key);
-            if (ok >= tau) e[ne++] = composite_key(ok, flat_base + (uint32_t)c);
-          }
-        }
+    for (int q = 0; q < kRegC / 4; ++q) {
+      const int i = 4 * (tid + 256 * q);
+      floatx4 x;
+      if (i + 3 < cnt) {
+        x = *(const floatx4*)(lprow + i);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = i + e < cnt ? lprow[i + e] : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rr.lp[4 * q + e] = x[e];
+    }
+  } else if constexpr (L == kFullScalar) {
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      const int i = tid + 256 * k;
+      rr.lp[k] = i < cnt ? lprow[i] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      const int i = tid + 256 * k;
+      rr.code[k] = i < cnt ? codes[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      const bool in_row = tid + 256 * k < cnt;
+      const bool ok = in_row && (unsigned)rr.code[k] < (unsigned)a.C;
+      if (in_row && !ok) fl |= GRW_FLAG_BAD_NODE;   // corrupt trie row: never read outside the row
+      rr.lp[k] = ok ? lprow[rr.code[k]] : 0.0f;
+      if (!ok) rr.code[k] = -1;
+    }
+  }
+}
+
+// Ordered key of candidate k of a loaded row (0 when it is not a candidate or is below
+// tau), with the precondition flags.
+template <int L>
+__device__ __forceinline__ uint32_t row_key(const RowRegs<L>& rr, int k, int cnt, float s, uint32_t tau, int& fl) {
+  if (!rr.valid(k, cnt)) return 0u;
+  const float lp = rr.lp[k];
+  if (__builtin_isnan(lp)) { fl |= GRW_FLAG_NAN_LOGPROB; return 0u; }
+  if (lp > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
+  const float key = s + lp;
+  if (key == -INFINITY) return 0u;
+  const uint32_t o = ordered_key(key);
+  return o >= tau ? o : 0u;
+}
+
+// The best candidate of a row of up to kOnePass candidates (0 when none).
+template <int L>
+__device__ __forceinline__ uint64_t row_best(const SelArgs& a, const float* lprow, const int32_t* codes, int cnt,
+                                             float s, uint32_t flat_base, int& fl) {
+  RowRegs<L> rr;
+  load_row<L>(rr, a, lprow, codes, cnt, fl);
+  uint64_t best = 0;
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) {
+    const uint32_t o = row_key<L>(rr, k, cnt, s, 0u, fl);
+    if (o) best = max(best, composite_key(o, flat_base + (uint32_t)rr.code_of(k)));
+  }
+  return best;
+}
+
+// The row layout of a beam's one-read path.
+__device__ __forceinline__ int row_layout(const SelArgs& a, const int32_t* codes, const float* lprow) {
+  if (codes != nullptr) return kTrie;
+  return ((a.C & 3) == 0 && (((uintptr_t)lprow) & 15) == 0) ? kFull : kFullScalar;
+}
+
+// Device-coherent access to data that another workgroup, possibly on another XCD, writes
+// or reads during the same kernel (relaxed agent-scope atomics: no cache maintenance).
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's stores are acknowledged at device scope
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// --------------------------------------------------------------------------------------
+// pilots and the request bound
+// --------------------------------------------------------------------------------------
+// One workgroup per pilot; descriptor {beam slot, request, first pilot-buffer entry,
+// threads per group}.  Each pilot contributes one candidate per group of threads (at most
+// top_k of its beam) with device-coherent stores and counts itself; the request's last
+// pilot sets bound[r] to the W_r-th best key of all contributions (0 when there are fewer
+// than W_r) and resets the count.
+__global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
+  __shared__ uint64_t red64[4];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scr[4];
+  __shared__ uint32_t red32[8];
+  __shared__ int red[4];
+  __shared__ int last_s;
+  const int tid = threadIdx.x;
+  const int4 pd = ((const int4*)a.pilot_desc)[blockIdx.x];
+  const int slot = pd.x, r = pd.y, gsz = pd.w;
+  const ReqDesc rd = a.req[r];
+  const float s = a.scores[slot];
+  const uint32_t flat_base = (uint32_t)(slot - rd.boff) * (uint32_t)a.C;
+  const float* lprow = a.logprobs + (size_t)slot * a.C;
+  int cnt = a.C, fl = 0;
+  const int32_t* codes = nullptr;
+  uint64_t best = 0;
+  if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes)) {
+    if (cnt <= kOnePass) {
+      const int lay = row_layout(a, codes, lprow);
+      if (lay == kFull) best = row_best<kFull>(a, lprow, codes, cnt, s, flat_base, fl);
+      else if (lay == kFullScalar) best = row_best<kFullScalar>(a, lprow, codes, cnt, s, flat_base, fl);
+      else best = row_best<kTrie>(a, lprow, codes, cnt, s, flat_base, fl);
+    } else {
+      for (int q = tid; q < cnt; q += 256) {
+        const int c = codes ? codes[q] : q;
+        if ((unsigned)c >= (unsigned)a.C) continue;
+        best = max(best, candidate(s, lprow[c], flat_base + (uint32_t)c, fl));
       }
     }
-    block_append<4>(buf, &cnt_s, e, ne);
-    __syncthreads();
-    n = cnt_s;
   }
-  if (fl) atomicOr(&flag_s, fl);
+  // one contribution per group of gsz threads (at most top_k per beam)
+  const int gl = gsz < 64 ? gsz : 64;
+  for (int o = 1; o < gl; o <<= 1) best = max(best, shfl_xor_u64(best, o));
+  if (gsz > 64) {
+    if ((tid & 63) == 0) red64[tid >> 6] = best;
+    __syncthreads();
+    const int w0 = (tid >> 6) & ~((gsz >> 6) - 1);
+    best = red64[w0];
+    for (int w = 1; w < (gsz >> 6); ++w) best = max(best, red64[w0 + w]);
+  }
+  if (tid % gsz == 0) st_dev(&a.pilot_buf[pd.z + tid / gsz], best);
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(rd.n_pilot - 1);
+  __syncthreads();
+  if (!last_s) return;
+  // the W_r-th best key of all contributions bounds the request's W_r-th best pool entry
+  constexpr int NP = kPilotCap / 256;
+  const int n_ent = rd.n_pilot * (256 / gsz);
+  const uint64_t* pb = a.pilot_buf + rd.pilot_off;
+  uint32_t pk[NP];
+  int nv = 0;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int q = tid + 256 * k;
+    pk[k] = q < n_ent ? (uint32_t)(ld_dev(&pb[q]) >> 32) : 0u;
+    nv += pk[k] != 0u;
+  }
+  nv = block_sum256(nv, red);
+  uint32_t lo = 0;
+  if (nv >= rd.W)
+    lo = regs_select32<256, NP>([&](int k) { return pk[k]; }, (uint32_t)rd.W, (uint32_t)nv, hist, scr, red32).v;
+  if (tid == 0) {
+    a.bound[r] = lo;
+    a.pilot_count[r] = 0u;
+  }
+}
 
-  // survivors: the top min(n, K) entries
-  uint64_t T = 0;
-  int n_surv = n;
-  if (n > K) {
-    T = block_select_threshold<256>([&](int i) { return buf[i]; }, n, K, hist, scr);
-    n_surv = K;
+// --------------------------------------------------------------------------------------
+// per-beam top-k
+// --------------------------------------------------------------------------------------
+// Rows of any length (used when C > kOnePass): rows of up to kOnePass candidates in
+// registers as above; longer rows stream through the LDS buffer.
+__global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
+  __shared__ uint64_t buf[kSelCap];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scr[4];
+  __shared__ uint64_t red64[8];
+  __shared__ int red[4];
+  __shared__ int cnt_s;
+  const int tid = threadIdx.x;
+  const int slot = blockIdx.x;
+  const int r = a.slot_req[slot];
+  const ReqDesc rd = a.req[r];
+  const int j = slot - rd.boff;
+  const float s = a.scores[slot];
+  int fl = 0;
+  int cnt = 0;
+  const int32_t* codes = nullptr;
+  uint32_t tau = a.bound[r];
+  // a beam below the bound keeps nothing: no key exceeds its beam's score
+  bool live = s != -INFINITY && !__builtin_isnan(s) && ordered_key(s) >= tau;
+  if (__builtin_isnan(s)) fl |= GRW_FLAG_NAN_LOGPROB;
+  if (live && !beam_row(a, slot, cnt, codes)) {
+    fl |= GRW_FLAG_BAD_NODE;
+    live = false;
   }
-  if (n_surv > 0) {
-    // lower bound of the request's W-th best key: this beam's own W-th best survivor
-    if (n_surv >= rd.W) {
-      uint64_t TW;
-      if (n_surv == rd.W && n > K) TW = T;
-      else TW = block_select_threshold<256>([&](int i) { return buf[i]; }, n, rd.W, hist, scr);
-      if (tid == 0) atomicMax(&a.bound[r], (uint32_t)(TW >> 32));
+  const float* lprow = a.logprobs + (size_t)slot * a.C;
+  const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
+  uint64_t* region = a.pool + rd.pool_off + (size_t)j * rd.K;
+  const int K = rd.K;
+  int n_out = 0;
+
+  if (live && cnt <= kOnePass) {
+    // ---- one pass: the row in registers, filtered by the bound, top K kept ----
+    uint64_t v[kRegC];
+    {
+      RowRegs<kTrie> rr;     // row positions t + 256 k, codes kept (also for the full range)
+      if (codes != nullptr) {
+        load_row<kTrie>(rr, a, lprow, codes, cnt, fl);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kRegC; ++k) {
+          const int i = tid + 256 * k;
+          rr.code[k] = i < cnt ? i : -1;
+          rr.lp[k] = i < cnt ? lprow[i] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k) {
+        const uint32_t o = row_key<kTrie>(rr, k, cnt, s, 0u, fl);
+        v[k] = o ? composite_key(o, flat_base + (uint32_t)rr.code[k]) : 0ull;
+      }
     }
-    if (tid == 0) pos_s = atomicAdd(&a.pool_count[r], (uint32_t)n_surv);
-    __syncthreads();
-    uint64_t* dst = a.pool + rd.pool_off + pos_s;
+    int na = 0;
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      if ((uint32_t)(v[k] >> 32) < tau) v[k] = 0;
+      na += v[k] != 0;
+    }
+    const int n = block_sum256(na, red);
+    if (n > 0) {
+      uint64_t T = 1;
+      n_out = n;
+      if (n > K) {
+        T = regs_select_threshold<256, kRegC>([&](int k) { return v[k]; }, K, hist, scr, red64);
+        n_out = K;
+      }
+      if (n_out >= rd.W) {                       // this beam alone bounds the request's W-th best
+        const uint64_t TW = (n_out == rd.W) ? T : regs_select_threshold<256, kRegC>([&](int k) { return v[k]; }, rd.W, hist, scr, red64);
+        if (tid == 0) atomicMax(&a.bound[r], (uint32_t)(TW >> 32));
+      }
+      int ns = 0;
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k) ns += (v[k] != 0 && v[k] >= T);
+      int total;
+      int p = block_excl_scan256(ns, red, &total);
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k)
+        if (v[k] != 0 && v[k] >= T) region[p++] = v[k];
+      n_out = min(total, K);                     // the entries written (n_out by construction)
+    }
+  } else if (live) {
+    // ---- long rows: stream through the LDS buffer ----
     if (tid == 0) cnt_s = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += 1024) {
+    int n = 0;
+    for (int base = 0; base < cnt; base += kSelChunk) {
+      if (n + kSelChunk > kSelCap) {             // buffer full: keep the top K, raise tau
+        const uint64_t T = block_select_threshold<256>([&](int i) { return buf[i]; }, n, K, hist, scr);
+        n = block_compact_ge(buf, n, T, &cnt_s);
+        const uint32_t tk = (uint32_t)(T >> 32);
+        tau = max(tau, tk);
+        tau = max(tau, __hip_atomic_load(&a.bound[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
       uint64_t e[4];
       int ne = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int i = base + tid + 256 * k;
-        if (i < n && buf[i] >= T) e[ne++] = buf[i];
-      }
-      block_append<4>(dst, &cnt_s, e, ne);
-    }
-  }
-  __syncthreads();
-  if (tid == 0 && flag_s) atomicOr(a.flags, flag_s);
-}
-
-__global__ __launch_bounds__(1024) void select_global_kernel(SelArgs a) {
-  __shared__ uint64_t sel[kMaxW];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scr[4];
-  __shared__ int cnt_s;
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const ReqDesc rd = a.req[r];
-  const int n = (int)a.pool_count[r];
-  const uint64_t* pool = a.pool + rd.pool_off;
-  const int W = rd.W;
-  const int nsel = min(n, W);
-  uint64_t T = 0;
-  if (n > W) T = block_select_threshold<1024>([&](int i) { return pool[i]; }, n, W, hist, scr);
-  if (tid == 0) cnt_s = 0;
-  __syncthreads();
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + tid;
-    uint64_t e[1];
-    int ne = 0;
-    if (i < n) {
-      const uint64_t v = pool[i];
-      if (v >= T) e[ne++] = v;
-    }
-    block_append<1>(sel, &cnt_s, e, ne);
-  }
-  __syncthreads();
-  int npow = 1;
-  while (npow < nsel) npow <<= 1;
-  for (int i = nsel + tid; i < npow; i += 1024) sel[i] = 0ull;   // sorts last
-  __syncthreads();
-  for (int k = 2; k <= npow; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < npow; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = sel[i], y = sel[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            sel[i] = y;
-            sel[ixj] = x;
+        if (i < cnt) {
+          const int c = codes ? codes[i] : i;
+          if ((unsigned)c >= (unsigned)a.C) {      // corrupt trie row: never read outside the row
+            fl |= GRW_FLAG_BAD_NODE;
+            continue;
           }
+          const uint64_t x = candidate(s, lprow[c], flat_base + (uint32_t)c, fl);
+          if (x != 0 && (uint32_t)(x >> 32) >= tau) e[ne++] = x;
         }
+      }
+      block_append<4>(buf, &cnt_s, e, ne);
+      __syncthreads();
+      n = cnt_s;
+    }
+    uint64_t T = 1;
+    n_out = n;
+    if (n > K) {
+      T = block_select_threshold<256>([&](int i) { return buf[i]; }, n, K, hist, scr);
+      n_out = K;
+    }
+    if (n_out > 0) {
+      if (n_out >= rd.W) {
+        const uint64_t TW = (n_out == rd.W && n > K)
+            ? T : block_select_threshold<256>([&](int i) { return buf[i]; }, n, rd.W, hist, scr);
+        if (tid == 0) atomicMax(&a.bound[r], (uint32_t)(TW >> 32));
+      }
+      if (tid == 0) cnt_s = 0;
+      __syncthreads();
+      for (int base = 0; base < n; base += 1024) {
+        uint64_t e[4];
+        int ne = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = base + tid + 256 * k;
+          if (i < n && buf[i] >= T) e[ne++] = buf[i];
+        }
+        block_append<4>(region, &cnt_s, e, ne);
       }
       __syncthreads();
+      n_out = min(cnt_s, K);                     // the entries written (n_out by construction)
     }
   }
+  if (tid == 0) a.surv_count[slot] = n_out;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
+}
+
+// --------------------------------------------------------------------------------------
+// global W-of-pool select
+// --------------------------------------------------------------------------------------
+// Output slot `rank` of the request: token, parent, exact score, trie child.
+__device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int rank, uint64_t v) {
   const int C = a.C;
-  for (int i = tid; i < W; i += 1024) {
-    const int slot = rd.boff + i;
-    if (i < nsel) {
-      const uint32_t flat = composite_flat(sel[i]);
-      const uint32_t b = flat / (uint32_t)C;
-      const int c = (int)(flat - b * (uint32_t)C);
-      const int ps = rd.boff + (int)b;
-      const float score = a.scores[ps] + a.logprobs[(size_t)ps * C + c];
-      int node = -1;
-      if (a.row_ptr != nullptr) {
-        const int pn = a.nodes[ps];
-        int lo = a.row_ptr[pn], hi = a.row_ptr[pn + 1] - 1;
-        node = -1;
-        while (lo <= hi) {
-          const int mid = (lo + hi) >> 1;
-          const int cm = a.code[mid];
-          if (cm == c) { node = mid + 1; break; }
-          if (cm < c) lo = mid + 1; else hi = mid - 1;
-        }
-        if (node < 0) atomicOr(a.flags, (int)GRW_FLAG_CHILD_MISSING);
-      }
-      a.out_token[slot] = c;
-      a.out_parent[slot] = (int)b;
-      a.out_score[slot] = score;
-      a.out_node[slot] = node;
-    } else {
-      a.out_token[slot] = -1;
-      a.out_parent[slot] = -1;
-      a.out_score[slot] = -INFINITY;
-      a.out_node[slot] = -1;
+  const int slot = rd.boff + rank;
+  const uint32_t flat = composite_flat(v);
+  const uint32_t b = flat / (uint32_t)C;
+  const int c = (int)(flat - b * (uint32_t)C);
+  if (b >= (uint32_t)rd.W) {                     // never for entries the per-beam stage wrote
+    atomicOr(a.flags, (int)GRW_FLAG_POOL_CORRUPT);
+    a.out_token[slot] = -1;
+    a.out_parent[slot] = -1;
+    a.out_score[slot] = -INFINITY;
+    a.out_node[slot] = -1;
+    return;
+  }
+  const int ps = rd.boff + (int)b;
+  const float score = a.scores[ps] + a.logprobs[(size_t)ps * C + c];
+  int node = -1;
+  if (a.row_ptr != nullptr) {
+    const int pn = a.nodes[ps];
+    int lo = a.row_ptr[pn], hi = a.row_ptr[pn + 1] - 1;
+    while (lo <= hi) {
+      const int mid = (lo + hi) >> 1;
+      const int cm = a.code[mid];
+      if (cm == c) { node = mid + 1; break; }
+      if (cm < c) lo = mid + 1; else hi = mid - 1;
     }
+    if (node < 0) atomicOr(a.flags, (int)GRW_FLAG_CHILD_MISSING);
+  }
+  a.out_token[slot] = c;
+  a.out_parent[slot] = (int)b;
+  a.out_score[slot] = score;
+  a.out_node[slot] = node;
+}
+
+// Histogram bin of an entry: ordered-key distance below the origin, scaled down by
+// `shift`, clamped to the NB bins.  Non-increasing in the entry, so the bins order the
+// entries (ties inside a bin are ranked by full comparison).
+template <int NB>
+__device__ __forceinline__ int hist_bin(uint64_t v, uint32_t origin, uint32_t shift) {
+  const uint32_t ok = (uint32_t)(v >> 32);
+  const uint32_t d = origin > ok ? origin - ok : 0u;
+  const uint32_t b = d >> shift;
+  return b < (uint32_t)NB ? (int)b : NB - 1;
+}
+
+// beam of entry index i: the last b with pre[b] <= i (pre[0] = 0, pre[W] = n > i)
+__device__ __forceinline__ int entry_beam(const uint32_t* pre, int W, uint32_t i) {
+  int lo = 0, hi = W - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// LDS of the W-of-pool select: beam prefix (MAXW + 1), bin counts / cursors (NB), bin
+// starts (NB + 1), winner array (WINCAP), radix histogram and small scratch.
+template <int NT, int NB, int MAXW, int WINCAP>
+struct FinalLds {
+  uint32_t pre[MAXW + 1];
+  uint32_t hcnt[NB];
+  uint32_t start[NB + 1];
+  uint64_t win[WINCAP];
+  uint32_t hist[256];
+  uint32_t scr[4];
+  uint32_t wsum[NT / 64];
+  uint32_t wmax[NT / 64];
+  uint32_t tb, maxc;
+  int cnt;
+};
+
+// The W_r-of-pool select of request r by one workgroup of NT threads (W_r <= MAXW).  The
+// beams' survivor counts place every pool entry in one index range; a histogram of the
+// entries' keys (bins measured down from the best live score, scaled so that the bound
+// falls inside the range) finds the bin of the W_r-th best entry; the entries of that bin
+// and of all better bins are placed bin by bin and ranked inside their bin, which gives
+// every winner its output position.  When a bin holds more than BINCAP entries, a radix
+// select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
+// device-coherent loads (they may come from other workgroups of the same kernel).
+template <int NT, int NB, int MAXW, int WINCAP, int BINCAP>
+__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP>& L) {
+  constexpr int BPT = MAXW / NT;     // beams per thread
+  constexpr int HPT = NB / NT;       // bins per thread
+  constexpr int NRG = 8;             // pool entries cached per thread (and per batch beyond)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ReqDesc rd = a.req[r];
+  const int W = rd.W, K = rd.K;
+  const uint64_t* pool = a.pool + rd.pool_off;
+
+  // beam prefix of the survivor counts, best live score
+  uint32_t cb[BPT];
+  uint32_t csum = 0, smax = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int b = tid * BPT + k;
+    cb[k] = b < W ? min((uint32_t)ld_dev(&a.surv_count[rd.boff + b]), (uint32_t)K) : 0u;
+    csum += cb[k];
+    if (b < W) {
+      const float sc = a.scores[rd.boff + b];
+      if (sc != -INFINITY && !__builtin_isnan(sc)) smax = max(smax, ordered_key(sc));
+    }
+  }
+  {
+    const uint32_t incl = (uint32_t)wave_inclusive_scan((int)csum);
+    const uint32_t m = wave_max(smax);
+    __syncthreads();
+    if (lane == 63) L.wsum[wave] = incl;
+    if (lane == 0) L.wmax[wave] = m;
+    if (tid == 0) { L.tb = NB; L.maxc = 0; }
+    __syncthreads();
+    uint32_t run = incl - csum;
+    for (int w = 0; w < wave; ++w) run += L.wsum[w];
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int b = tid * BPT + k;
+      if (b < W) L.pre[b] = run;
+      run += cb[k];
+      if (b == W - 1) L.pre[W] = run;
+    }
+    smax = 0;
+    for (int w = 0; w < NT / 64; ++w) smax = max(smax, L.wmax[w]);
+  }
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) L.hcnt[tid * HPT + k] = 0u;
+  __syncthreads();
+  const uint32_t n = L.pre[W];
+  const int nsel = min((int)n, W);
+
+  // histogram origin and scale: bins reach from the best live score down to the bound
+  uint32_t lo = ld_dev(&a.bound[r]);
+  if (lo == 0 && smax != 0) {
+    const uint32_t u = (smax & 0x80000000u) ? (smax & 0x7fffffffu) : ~smax;   // inverse ordered key
+    lo = ordered_key(__uint_as_float(u) - 64.0f);
+  }
+  const uint32_t span = smax > lo ? smax - lo : 0u;
+  uint32_t shift = 0;
+  while ((span >> shift) >= (uint32_t)NB - 1) ++shift;
+
+  auto entry = [&](uint32_t i) {
+    const int b = entry_beam(L.pre, W, i);
+    return ld_dev(&pool[(size_t)b * K + (i - L.pre[b])]);
+  };
+  const bool cached = n <= (uint32_t)(NT * NRG);
+  uint64_t ev[NRG];
+#pragma unroll
+  for (int k = 0; k < NRG; ++k) {
+    const uint32_t i = tid + NT * k;
+    ev[k] = (cached && i < n) ? entry(i) : 0;
+  }
+  // entries beyond the register cache are read in batches of NRG per thread
+  auto for_each_entry = [&](auto&& fn) {
+    if (cached) {
+#pragma unroll
+      for (int k = 0; k < NRG; ++k)
+        if (ev[k]) fn(ev[k]);
+    } else {
+      for (uint32_t base = 0; base < n; base += NT * NRG) {
+        uint64_t bv[NRG];
+#pragma unroll
+        for (int k = 0; k < NRG; ++k) {
+          const uint32_t i = base + tid + NT * k;
+          bv[k] = i < n ? entry(i) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < NRG; ++k)
+          if (bv[k]) fn(bv[k]);
+      }
+    }
+  };
+  for_each_entry([&](uint64_t v) { atomicAdd(&L.hcnt[hist_bin<NB>(v, smax, shift)], 1u); });
+  __syncthreads();
+
+  // bin starts: exclusive scan of the histogram; the bin of the nsel-th entry
+  uint32_t c[HPT];
+  {
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) { c[k] = L.hcnt[tid * HPT + k]; tsum += c[k]; }
+    const uint32_t incl = (uint32_t)wave_inclusive_scan((int)tsum);
+    __syncthreads();
+    if (lane == 63) L.wsum[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - tsum;
+    for (int w = 0; w < wave; ++w) run += L.wsum[w];
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      L.start[tid * HPT + k] = run;
+      if (nsel > 0 && run < (uint32_t)nsel && (uint32_t)nsel <= run + c[k]) L.tb = tid * HPT + k;
+      run += c[k];
+    }
+    if (tid == NT - 1) L.start[NB] = run;
   }
   __syncthreads();
+  const uint32_t tb = L.tb;
+  {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k)
+      if ((uint32_t)(tid * HPT + k) <= tb) m = max(m, c[k]);
+    m = wave_max(m);
+    if (lane == 0 && m) atomicMax(&L.maxc, m);
+  }
+  __syncthreads();
+  const bool fast = nsel > 0 && tb < (uint32_t)NB && L.maxc <= (uint32_t)BINCAP && L.start[tb + 1] <= (uint32_t)WINCAP;
+
+  if (fast) {
+    // place every entry of bins <= tb in its bin's segment, then rank it inside the bin
+    uint32_t* cursor = L.hcnt;
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) cursor[tid * HPT + k] = 0u;
+    __syncthreads();
+    auto place = [&](uint64_t v) {
+      const int b = hist_bin<NB>(v, smax, shift);
+      if ((uint32_t)b <= tb) {
+        const uint32_t p = L.start[b] + atomicAdd(&cursor[b], 1u);
+        if (p < L.start[b + 1]) L.win[p] = v;
+      }
+    };
+    for_each_entry(place);
+    __syncthreads();
+    const int m = (int)L.start[tb + 1];
+    for (int p = tid; p < m; p += NT) {
+      const uint64_t v = L.win[p];
+      const int b = hist_bin<NB>(v, smax, shift);
+      const int s0 = (int)L.start[b], e0 = (int)L.start[b + 1];
+      int rank = s0;
+      for (int q = s0; q < e0; ++q) rank += L.win[q] > v;
+      if (rank < nsel) emit(a, rd, rank, v);
+    }
+  } else if (nsel > 0) {
+    // fallback: radix select of the W-th entry, gather, bitonic sort
+    uint64_t T = 0;
+    if ((int)n > W) T = block_select_threshold<NT>([&](int i) { return entry((uint32_t)i); }, (int)n, W, L.hist, L.scr);
+    if (tid == 0) L.cnt = 0;
+    __syncthreads();
+    for (uint32_t base = 0; base < n; base += NT) {
+      const uint32_t i = base + tid;
+      uint64_t e[1];
+      int ne = 0;
+      if (i < n) {
+        const uint64_t v = entry(i);
+        if (v >= T) e[ne++] = v;
+      }
+      block_append<1>(L.win, &L.cnt, e, ne);
+    }
+    __syncthreads();
+    int npow = 1;
+    while (npow < nsel) npow <<= 1;
+    for (int i = nsel + tid; i < npow; i += NT) L.win[i] = 0ull;   // sorts last
+    __syncthreads();
+    for (int k = 2; k <= npow; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int i = tid; i < npow; i += NT) {
+          const int ixj = i ^ jj;
+          if (ixj > i) {
+            const uint64_t x = L.win[i], y = L.win[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? (x < y) : (x > y)) {
+              L.win[i] = y;
+              L.win[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < nsel; i += NT) emit(a, rd, i, L.win[i]);
+  }
+  for (int i = nsel + tid; i < W; i += NT) {
+    const int slot = rd.boff + i;
+    a.out_token[slot] = -1;
+    a.out_parent[slot] = -1;
+    a.out_score[slot] = -INFINITY;
+    a.out_node[slot] = -1;
+  }
+}
+
+constexpr int kGlobThreads = 1024;
+constexpr int kGlobWinCap = kMaxW + kBinCap;
+typedef FinalLds<kGlobThreads, kHistBins, kMaxW, kGlobWinCap> GlobLds;
+
+__global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GlobLds& L = *(GlobLds*)smem;
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap>(a, blockIdx.x, L);
+  if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
+}
+
+// --------------------------------------------------------------------------------------
+// per-beam top-k and the W-of-pool select in one kernel
+// --------------------------------------------------------------------------------------
+// Used when every row fits the one-read path (C <= kOnePass) and W <= kFusedMaxW, after
+// select_pilot has set the bounds.  One workgroup per beam slot; survivors and counts are
+// stored device-coherently, each slot counts itself done, and the workgroup that completes
+// a request runs its W-of-pool select and resets the request's step state.
+constexpr int kFusedMaxW = 1024;
+constexpr int kFusedBins = 1024;
+constexpr int kFusedBinCap = 512;
+constexpr int kFusedWinCap = kFusedMaxW + kFusedBinCap;
+typedef FinalLds<256, kFusedBins, kFusedMaxW, kFusedWinCap> FusedLds;
+
+struct BeamRow {
+  int slot, r, cnt;
+  float s;
+  bool live;
+  uint32_t tau;        // the request's bound
+  ReqDesc rd;
+  const int32_t* codes;
+  const float* lprow;
+};
+
+__device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& fl) {
+  BeamRow b;
+  b.slot = slot;
+  b.r = a.slot_req[slot];
+  b.s = a.scores[slot];
+  b.rd = a.req[b.r];           // descriptor and bound are read before the row
+  b.tau = a.bound[b.r];
+  b.cnt = a.C;
+  b.codes = nullptr;
+  b.lprow = a.logprobs + (size_t)slot * a.C;
+  b.live = b.s != -INFINITY && !__builtin_isnan(b.s);
+  if (__builtin_isnan(b.s)) fl |= GRW_FLAG_NAN_LOGPROB;
+  if (b.live && !beam_row(a, slot, b.cnt, b.codes)) {
+    fl |= GRW_FLAG_BAD_NODE;
+    b.live = false;
+  }
+  if (b.live && b.cnt > kOnePass) {              // longer than the code range: corrupt row
+    fl |= GRW_FLAG_BAD_NODE;
+    b.live = false;
+  }
+  return b;
+}
+
+// Survivors of one loaded beam row: candidates >= the request's bound, at most K of them
+// (radix select over the registers), stored device-coherently in the beam's pool region.
+// Publishes the beam's own W_r-th best when it alone holds >= W_r survivors.  Returns the
+// survivor count.  Reached by every thread of the workgroup.
+template <int L>
+__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L>& rr, int& fl, uint32_t* hist,
+                         uint32_t* scr, uint32_t* red32, int* red) {
+  const ReqDesc& rd = b.rd;
+  const uint32_t tau = b.tau;
+  // a beam below the bound keeps nothing: no key exceeds its beam's score
+  if (!b.live || ordered_key(b.s) < tau) return 0;
+  const int j = b.slot - rd.boff;
+  const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
+  auto flat = [&](int k) -> uint32_t {
+    uint32_t fb = flat_base;
+    asm volatile("" : "+v"(fb));
+    return fb + (uint32_t)rr.code_of(k);
+  };
+  uint32_t ok[kRegC];
+  int na = 0;
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) {
+    ok[k] = row_key<L>(rr, k, b.cnt, b.s, tau, fl);
+    na += ok[k] != 0u;
+  }
+  auto key = [&](int k) -> uint32_t { return ok[k]; };
+  int n;
+  int p = block_excl_scan256(na, red, &n);      // offsets, valid while every candidate is kept
+  if (n == 0) return 0;
+  const int K = rd.K;
+  uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
+  if (n <= K && n < rd.W) {
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k)
+      if (ok[k]) st_dev(&region[p++], composite_key(ok[k], flat(k)));
+    return n;
+  }
+  uint64_t T = 1;
+  int n_out = n;
+  if (n > K) {
+    T = regs_select_composite<256, kRegC>(key, flat, K, n, hist, scr, red32);
+    n_out = K;
+  }
+  if (n_out >= rd.W) {                           // this beam alone bounds the request's W-th best
+    const uint64_t TW = (n_out == rd.W) ? T : regs_select_composite<256, kRegC>(key, flat, rd.W, n, hist, scr, red32);
+    if (threadIdx.x == 0) atomicMax(&a.bound[b.r], (uint32_t)(TW >> 32));
+  }
+  // survivors as a bit mask (keeps the 64-bit composites out of registers)
+  const uint32_t thi = (uint32_t)(T >> 32), tlo = (uint32_t)T;
+  uint32_t keep = 0;
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k)
+    if (ok[k] > thi || (ok[k] == thi && ok[k] != 0u && ~flat(k) >= tlo)) keep |= 1u << k;
+  int total;
+  p = block_excl_scan256(__builtin_popcount(keep), red, &total);
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k)
+    if ((keep >> k) & 1u) st_dev(&region[p++], composite_key(ok[k], flat(k)));
+  return min(total, K);     // the entries written (n_out by construction)
+}
+
+template <int L>
+__global__ __launch_bounds__(256) void select_fused_kernel(SelArgs a) {
+  __shared__ FusedLds fin;
+  __shared__ uint32_t red32[8];
+  __shared__ int red[4];
+  __shared__ int last_s;
+  const int tid = threadIdx.x;
+  const int slot = blockIdx.x;
+  int fl = 0;
+  const BeamRow b = beam_setup(a, slot, fl);
+  RowRegs<L> rr;
+  if (b.live) load_row<L>(rr, a, b.lprow, b.codes, b.cnt, fl);
+  const int n_out = keep_beam<L>(a, b, rr, fl, fin.hist, fin.scr, red32, red);
+  if (tid == 0) st_dev(&a.surv_count[slot], n_out);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
+
+  // ---- count the slot done; the workgroup completing its request selects the beams ----
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) last_s = atomicAdd(&a.done_count[b.r], 1u) + 1u == (uint32_t)a.req[b.r].W;
+  __syncthreads();
+  if (!last_s) return;
+  final_select<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap>(a, b.r, fin);
+  __syncthreads();
   if (tid == 0) {
-    a.pool_count[r] = 0u;
-    a.bound[r] = 0u;
+    a.done_count[b.r] = 0u;
+    a.bound[b.r] = 0u;
   }
 }
 
@@ -354,13 +1129,36 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 hipError_t launch_select_topk(const SelArgs& a, hipStream_t s) {
   if (a.sumW == 0) return hipSuccess;
+  select_pilot_kernel<<<a.n_pilots, 256, 0, s>>>(a);
   select_topk_kernel<<<a.sumW, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_global(const SelArgs& a, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  select_global_kernel<<<a.R, 1024, 0, s>>>(a);
+  static bool attr_set = false;   // the bin arrays and winner array exceed the default 64 KB
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)select_global_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GlobLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  select_global_kernel<<<a.R, kGlobThreads, sizeof(GlobLds), s>>>(a);
+  return hipGetLastError();
+}
+
+bool select_fused_ok(int C, int max_W) { return C <= kOnePass && max_W <= kFusedMaxW; }
+
+hipError_t launch_select_fused(const SelArgs& a, hipStream_t s) {
+  if (a.sumW == 0) return hipSuccess;
+  select_pilot_kernel<<<a.n_pilots, 256, 0, s>>>(a);
+  const int grid = a.sumW;
+  if (a.row_ptr != nullptr)
+    select_fused_kernel<kTrie><<<grid, 256, 0, s>>>(a);
+  else if ((a.C & 3) == 0 && (((uintptr_t)a.logprobs) & 15) == 0)
+    select_fused_kernel<kFull><<<grid, 256, 0, s>>>(a);
+  else
+    select_fused_kernel<kFullScalar><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -68,7 +68,8 @@ enum grw_device_flag {
   GRW_FLAG_POS_LOGPROB = 2,     /* a log-probability > 0 was seen (breaks the early exit)   */
   GRW_FLAG_BAD_NODE = 4,        /* a live beam's trie node is outside [0, n_internal)       */
   GRW_FLAG_BAD_PARENT = 8,      /* a parent pointer walk left [0, W_r)                       */
-  GRW_FLAG_CHILD_MISSING = 16   /* a selected code is not a child of its parent's node      */
+  GRW_FLAG_CHILD_MISSING = 16,  /* a selected code is not a child of its parent's node      */
+  GRW_FLAG_POOL_CORRUPT = 32    /* internal check: a pool entry names a slot outside W_r    */
 };
 
 /*
@@ -224,6 +225,12 @@ int grw_ws_error(grw_ws* ws, void* stream, int32_t* flags);
 /* Number of partial-result splits the shared stage uses for request r of the bound batch
    (diagnostics; host-side, no device work). */
 int grw_ws_splits(const grw_ws* ws, int32_t r, int32_t* n_splits);
+
+/* Size of request r's candidate pool after the last beam_select call: the survivors its
+   beams kept, after the per-beam top_k and the early-exit bound (xLLM design doc, section
+   4.1.1 for the beam_width x top_k pool, section 4.3 for stopping early).  Synchronises
+   the stream, then writes the count to *pool_size (host pointer).  Diagnostics only. */
+int grw_ws_pool_size(grw_ws* ws, int32_t r, void* stream, int64_t* pool_size);
 
 const char* grw_status_str(int status);
 

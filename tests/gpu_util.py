@@ -46,6 +46,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
     ws.beams_init(loop.scores[0], loop.nodes[0])
     check = list(range(R)) if check is None else list(check)
     state = {r: initial_beams(Ws[r]) for r in check}
+    pools = {}
     for d in range(S):
         lp = lp_of_step(d)
         loop.select_step(d, torch.from_numpy(np.ascontiguousarray(lp)).cuda())
@@ -72,9 +73,14 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
             else:
                 assert np.all(nd[a:a + W] == -1), where
             assert np.all(nd[a + n:a + W] == -1), where
+            # the kept pool holds every winner and at most W * K entries
+            pool = ws.pool_size(r)
+            assert n <= pool <= W * Ks[r], f"{where}: pool {pool} for {n} winners"
+            pools.setdefault(r, []).append(pool)
             state[r] = (res["scores"], res["prefixes"])
     flags = ws.error_flags()
     assert flags == 0, f"device flags {flags}"
+    loop.pool_sizes = pools
     return loop, ws
 
 

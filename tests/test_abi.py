@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("beam_attn_decode", "beam_select", "grw_ws_create", "grw_ws_destroy",
               "grw_ws_bind_batch", "grw_beams_init", "grw_backtrack", "grw_ws_error",
-              "grw_ws_splits", "grw_status_str"):
+              "grw_ws_splits", "grw_ws_pool_size", "grw_status_str"):
         assert n in names
 
 
@@ -72,3 +72,4 @@ def test_null_handles_rejected(clib):
     assert clib.beam_attn_decode(None, None, None, None, None, None, None, None, None, 0, None, None) == 1
     assert clib.beam_select(None, *([None] * 5), 0, 1, 1, 1, None, None, None, None, None) == 1
     assert clib.grw_backtrack(None, None, None, 1, None, None) == 1
+    assert clib.grw_ws_pool_size(None, 0, None, None) == 1

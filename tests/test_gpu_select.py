@@ -32,8 +32,21 @@ def test_wide512_unconstrained_full_pool(lib):
     wl = workload("wide512u")
     W, K, P = request_shapes(wl)
     say("[select] wide512u")
-    select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), None,
-                          check=[1], label="wide512u")
+    loop, ws = select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), None,
+                                     check=[1], label="wide512u")
+    # with every beam live, the pilot bound keeps a small part of the 262144-entry pool
+    assert loop.pool_sizes[1][-1] < int(W[1]) * int(K[1]) // 8, loop.pool_sizes
+
+
+def test_wide_requests_beyond_the_fused_limit(lib):
+    """W > 1024: pilot, per-beam and the 1024-thread global select kernels."""
+    rng = np.random.default_rng(7)
+    W, K, C, S = [1200, 1500], [16, 3], 500, 3
+    lps = [rng.normal(0.0, 2.0, size=(sum(W), C)) for _ in range(S)]
+    lps = [(x - np.log(np.exp(x).sum(axis=1, keepdims=True))).astype(np.float32) for x in lps]
+    lps = [np.minimum(x, 0.0) for x in lps]
+    say("[select] W > 1024")
+    select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wide-multi")
 
 
 def test_mixed_ragged_batch(lib):
