@@ -147,6 +147,56 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return r;
 }
 
+// Store a wave's 32 rows of normalised partial output and their LSE.  The partial output
+// goes out through LDS so that every store instruction writes whole rows (512 B per query
+// row): written straight from the MFMA layout, each instruction would put 32-byte pieces of
+// 32 rows.  Called once every wave is past its last tile (8 KB of smem per wave are free);
+// each wave stages its 32 rows x 64 dims (8 KB, 16-byte chunk c of row r at c ^ (r % 16))
+// twice.  out_scale multiplies the output (the fp8 V scale, else 1).
+__device__ __forceinline__ void store_partial(const AttnArgs& a, const ShWork& wk, const ReqDesc& rd, uint8_t* smem,
+                                              const floatx16 (&o)[DH / 32], float m_run, float l_run, bool row_ok,
+                                              int slot, int qh, float out_scale) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = a.g, Hq = a.Hq, h = wk.h;
+  const int nrows = rd.W * g;
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = row_ok ? out_scale / l : 0.0f;
+  if (row_ok && hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
+  uint8_t* tb = smem + wave * 8192;
+  const int rrow = lane >> 4, rch = lane & 15;   // read side: 4 rows of 16 chunks per instruction
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int db2 = 0; db2 < 2; ++db2) {
+      const int db = half * 2 + db2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = db2 * 8 + i * 2 + hi;
+        const floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
+                           o[db][i * 4 + 3] * inv};
+        *(floatx4*)(tb + l32 * 256 + ((ch ^ (l32 & 15)) << 4)) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + rrow;
+      const floatx4 v = *(const floatx4*)(tb + r * 256 + ((rch ^ (r & 15)) << 4));
+      const int mr = wk.m0 + wave * 32 + r;
+      if (mr < nrows) {
+        const int bb = mr / g;
+        const int qq = h * g + (mr - bb * g);
+        float* dst = a.opart + (((size_t)wk.split * a.sumW + rd.boff + bb) * Hq + qq) * DH;
+        *(floatx4*)(dst + half * 64 + rch * 4) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // reads done before the next half overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, const ShWork* __restrict__ work) {
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (K_TILE + V_TILE)];
@@ -293,20 +343,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
     __syncthreads();
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  if (!row_ok) return;
-  const float inv = vscale / l;
-  float* dst = a.opart + (((size_t)wk.split * a.sumW + slot) * Hq + qh) * DH;
-#pragma unroll
-  for (int db = 0; db < DH / 32; ++db) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
-                   o[db][i * 4 + 3] * inv};
-      *(floatx4*)(dst + db * 32 + i * 8 + hi * 4) = v;
-    }
-  }
-  if (hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
+  __syncthreads();   // every wave is past its last tile: the tile buffers are free
+  store_partial(a, wk, rd, (uint8_t*)smem, o, m_run, l_run, row_ok, slot, qh, vscale);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -488,50 +526,12 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_lds_kernel(AttnArg
     __builtin_amdgcn_s_setprio(0);
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = row_ok ? 1.0f / l : 0.0f;
-  if (row_ok && hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
-  // The partial output goes out through LDS so that every store instruction writes whole
-  // rows (512 B per query row): written straight from the MFMA layout, each instruction
-  // would put 32-byte pieces of 32 rows.  The ring is free once every wave is past its last
-  // tile; each wave stages its 32 rows x 64 dims (8 KB, 16-byte chunk c of row r at
-  // c ^ (r % 16)) twice.
-  __syncthreads();
-  uint8_t* tb = smem + wave * 8192;
-  const int rrow = lane >> 4, rch = lane & 15;   // read side: 4 rows of 16 chunks per instruction
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-#pragma unroll
-    for (int db2 = 0; db2 < 2; ++db2) {
-      const int db = half * 2 + db2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ch = db2 * 8 + i * 2 + hi;
-        const floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
-                           o[db][i * 4 + 3] * inv};
-        *(floatx4*)(tb + l32 * 256 + ((ch ^ (l32 & 15)) << 4)) = v;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * 4 + rrow;
-      const floatx4 v = *(const floatx4*)(tb + r * 256 + ((rch ^ (r & 15)) << 4));
-      const int mr = wk.m0 + wave * 32 + r;
-      if (mr < nrows) {
-        const int bb = mr / g;
-        const int qq = h * g + (mr - bb * g);
-        float* dst = a.opart + (((size_t)wk.split * a.sumW + rd.boff + bb) * Hq + qq) * DH;
-        *(floatx4*)(dst + half * 64 + rch * 4) = v;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // reads done before the next half overwrites
-    __builtin_amdgcn_wave_barrier();
-  }
+  __syncthreads();   // every wave is past its last tile: the ring is free
+  store_partial(a, wk, rd, smem, o, m_run, l_run, row_ok, slot, qh, 1.0f);
 }
 
 }  // namespace lds
+
 
 // ---------------------------------------------------------------------------------------
 // Generic VALU shared stage: one workgroup per (slot, query head, split), any dtype and
