@@ -31,6 +31,7 @@ struct grw_ws {
   float* d_ou = nullptr;
   float* d_lu = nullptr;
   uint64_t* d_pool = nullptr;
+  int32_t* d_pool_edge = nullptr;
   int64_t pool_cap = 0;
   int32_t* d_surv_count = nullptr;
   uint32_t* d_bound = nullptr;
@@ -85,6 +86,7 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_ou);
   (void)hipFree(w->d_lu);
   (void)hipFree(w->d_pool);
+  (void)hipFree(w->d_pool_edge);
   (void)hipFree(w->d_surv_count);
   (void)hipFree(w->d_bound);
   (void)hipFree(w->d_pilot_desc);
@@ -253,6 +255,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_ou, B * L.Hq * L.D);
   if (st == GRW_OK) st = dev_alloc(&w->d_lu, B * L.Hq);
   if (st == GRW_OK) st = dev_alloc(&w->d_pool, w->pool_cap);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pool_edge, w->pool_cap);
   if (st == GRW_OK) st = dev_alloc(&w->d_surv_count, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 4 * B);
@@ -485,6 +488,7 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
   a.R = w->R;
   a.pool = w->d_pool;
   a.surv_count = w->d_surv_count;
+  a.pool_edge = w->d_pool_edge;
   a.bound = w->d_bound;
   a.pilot_desc = w->d_pilot_desc;
   a.n_pilots = w->n_pilots;

@@ -49,6 +49,11 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float whose ordered key is k (for k = 0x7FFFFFFF, which no float maps to: -0.0).
+__device__ __forceinline__ float float_of_ordered(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Composite selection key: ordered score key in the high word, ~flat in the low word, so
 // that a larger composite means (key descending, flat ascending).
 __device__ __forceinline__ uint64_t composite_key(uint32_t okey, uint32_t flat) {

@@ -84,6 +84,7 @@ struct SelArgs {
   int32_t sumW, R;
   uint64_t* pool;           // per request: W_r regions of K_r entries (one per beam slot)
   int32_t* surv_count;      // [sumW] entries in each beam's pool region
+  int32_t* pool_edge;       // CSR edge of each pool entry (fused step with a trie)
   uint32_t* bound;          // [R] ordered-key lower bound of the W_r-th best key
   const int32_t* pilot_desc;   // [n_pilots][4] beam slot, request, first pilot-buffer entry,
                                // threads per group, of each pilot workgroup

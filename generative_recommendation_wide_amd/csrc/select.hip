@@ -333,6 +333,7 @@ struct RowRegs {
 };
 
 // Read a row of up to kOnePass candidates into registers (one load per candidate).
+// Positions that hold no candidate read as -inf.
 template <int L>
 __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const float* lprow,
                                          const int32_t* codes, int cnt, int& fl) {
@@ -346,7 +347,7 @@ __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const
         x = *(const floatx4*)(lprow + i);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = i + e < cnt ? lprow[i + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) x[e] = i + e < cnt ? lprow[i + e] : -INFINITY;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) rr.lp[4 * q + e] = x[e];
@@ -355,7 +356,7 @@ __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const
 #pragma unroll
     for (int k = 0; k < kRegC; ++k) {
       const int i = tid + 256 * k;
-      rr.lp[k] = i < cnt ? lprow[i] : 0.0f;
+      rr.lp[k] = i < cnt ? lprow[i] : -INFINITY;
     }
   } else {
 #pragma unroll
@@ -368,7 +369,7 @@ __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const
       const bool in_row = tid + 256 * k < cnt;
       const bool ok = in_row && (unsigned)rr.code[k] < (unsigned)a.C;
       if (in_row && !ok) fl |= GRW_FLAG_BAD_NODE;   // corrupt trie row: never read outside the row
-      rr.lp[k] = ok ? lprow[rr.code[k]] : 0.0f;
+      rr.lp[k] = ok ? lprow[rr.code[k]] : -INFINITY;
       if (!ok) rr.code[k] = -1;
     }
   }
@@ -663,7 +664,9 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
 // global W-of-pool select
 // --------------------------------------------------------------------------------------
 // Output slot `rank` of the request: token, parent, exact score, trie child.
-__device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int rank, uint64_t v) {
+// edge: the CSR edge of the entry when the per-beam stage recorded it (its child is node
+// edge + 1), else -1 (the child is then found by a binary search of the parent's row).
+__device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int rank, uint64_t v, int edge = -1) {
   const int C = a.C;
   const int slot = rd.boff + rank;
   const uint32_t flat = composite_flat(v);
@@ -680,7 +683,9 @@ __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int ra
   const int ps = rd.boff + (int)b;
   const float score = a.scores[ps] + a.logprobs[(size_t)ps * C + c];
   int node = -1;
-  if (a.row_ptr != nullptr) {
+  if (a.row_ptr != nullptr && edge >= 0) {
+    node = edge + 1;
+  } else if (a.row_ptr != nullptr) {
     const int pn = a.nodes[ps];
     int lo = a.row_ptr[pn], hi = a.row_ptr[pn + 1] - 1;
     while (lo <= hi) {
@@ -720,12 +725,13 @@ __device__ __forceinline__ int entry_beam(const uint32_t* pre, int W, uint32_t i
 
 // LDS of the W-of-pool select: beam prefix (MAXW + 1), bin counts / cursors (NB), bin
 // starts (NB + 1), winner array (WINCAP), radix histogram and small scratch.
-template <int NT, int NB, int MAXW, int WINCAP>
+template <int NT, int NB, int MAXW, int WINCAP, int EDGECAP = 1>
 struct FinalLds {
   uint32_t pre[MAXW + 1];
   uint32_t hcnt[NB];
   uint32_t start[NB + 1];
   uint64_t win[WINCAP];
+  int32_t wedge[EDGECAP];    // CSR edge of each placed entry (when EDGECAP == WINCAP)
   uint32_t hist[256];
   uint32_t scr[4];
   uint32_t wsum[NT / 64];
@@ -742,8 +748,9 @@ struct FinalLds {
 // every winner its output position.  When a bin holds more than BINCAP entries, a radix
 // select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
 // device-coherent loads (they may come from other workgroups of the same kernel).
-template <int NT, int NB, int MAXW, int WINCAP, int BINCAP>
-__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP>& L) {
+template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP>
+__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L) {
+  constexpr bool EDGES = EDGECAP == WINCAP;   // entries carry their CSR edge (trie rows)
   constexpr int BPT = MAXW / NT;     // beams per thread
   constexpr int HPT = NB / NT;       // bins per thread
   constexpr int NRG = 8;             // pool entries cached per thread (and per batch beyond)
@@ -805,34 +812,44 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
     const int b = entry_beam(L.pre, W, i);
     return ld_dev(&pool[(size_t)b * K + (i - L.pre[b])]);
   };
+  const bool edges = EDGES && a.row_ptr != nullptr;
+  const int32_t* pedge = a.pool_edge + rd.pool_off;
+  auto entry_edge = [&](uint32_t i) -> int {
+    const int b = entry_beam(L.pre, W, i);
+    return ld_dev(&pedge[(size_t)b * K + (i - L.pre[b])]);
+  };
   const bool cached = n <= (uint32_t)(NT * NRG);
   uint64_t ev[NRG];
+  int eg[NRG];
 #pragma unroll
   for (int k = 0; k < NRG; ++k) {
     const uint32_t i = tid + NT * k;
     ev[k] = (cached && i < n) ? entry(i) : 0;
+    eg[k] = (edges && cached && i < n) ? entry_edge(i) : -1;
   }
   // entries beyond the register cache are read in batches of NRG per thread
   auto for_each_entry = [&](auto&& fn) {
     if (cached) {
 #pragma unroll
       for (int k = 0; k < NRG; ++k)
-        if (ev[k]) fn(ev[k]);
+        if (ev[k]) fn(ev[k], eg[k]);
     } else {
       for (uint32_t base = 0; base < n; base += NT * NRG) {
         uint64_t bv[NRG];
+        int be[NRG];
 #pragma unroll
         for (int k = 0; k < NRG; ++k) {
           const uint32_t i = base + tid + NT * k;
           bv[k] = i < n ? entry(i) : 0;
+          be[k] = (edges && i < n) ? entry_edge(i) : -1;
         }
 #pragma unroll
         for (int k = 0; k < NRG; ++k)
-          if (bv[k]) fn(bv[k]);
+          if (bv[k]) fn(bv[k], be[k]);
       }
     }
   };
-  for_each_entry([&](uint64_t v) { atomicAdd(&L.hcnt[hist_bin<NB>(v, smax, shift)], 1u); });
+  for_each_entry([&](uint64_t v, int) { atomicAdd(&L.hcnt[hist_bin<NB>(v, smax, shift)], 1u); });
   __syncthreads();
 
   // bin starts: exclusive scan of the histogram; the bin of the nsel-th entry
@@ -874,11 +891,14 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
 #pragma unroll
     for (int k = 0; k < HPT; ++k) cursor[tid * HPT + k] = 0u;
     __syncthreads();
-    auto place = [&](uint64_t v) {
+    auto place = [&](uint64_t v, int e) {
       const int b = hist_bin<NB>(v, smax, shift);
       if ((uint32_t)b <= tb) {
         const uint32_t p = L.start[b] + atomicAdd(&cursor[b], 1u);
-        if (p < L.start[b + 1]) L.win[p] = v;
+        if (p < L.start[b + 1]) {
+          L.win[p] = v;
+          if constexpr (EDGES) L.wedge[p] = e;
+        }
       }
     };
     for_each_entry(place);
@@ -890,7 +910,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
       const int s0 = (int)L.start[b], e0 = (int)L.start[b + 1];
       int rank = s0;
       for (int q = s0; q < e0; ++q) rank += L.win[q] > v;
-      if (rank < nsel) emit(a, rd, rank, v);
+      if (rank < nsel) emit(a, rd, rank, v, EDGES ? L.wedge[p] : -1);
     }
   } else if (nsel > 0) {
     // fallback: radix select of the W-th entry, gather, bitonic sort
@@ -942,12 +962,12 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
 
 constexpr int kGlobThreads = 1024;
 constexpr int kGlobWinCap = kMaxW + kBinCap;
-typedef FinalLds<kGlobThreads, kHistBins, kMaxW, kGlobWinCap> GlobLds;
+typedef FinalLds<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, 1> GlobLds;
 
 __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GlobLds& L = *(GlobLds*)smem;
-  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap>(a, blockIdx.x, L);
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1>(a, blockIdx.x, L);
   if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
 }
 
@@ -962,10 +982,11 @@ constexpr int kFusedMaxW = 1024;
 constexpr int kFusedBins = 1024;
 constexpr int kFusedBinCap = 512;
 constexpr int kFusedWinCap = kFusedMaxW + kFusedBinCap;
-typedef FinalLds<256, kFusedBins, kFusedMaxW, kFusedWinCap> FusedLds;
+typedef FinalLds<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedWinCap> FusedLds;
 
 struct BeamRow {
   int slot, r, cnt;
+  int beg;             // first CSR edge of the beam's trie row
   float s;
   bool live;
   uint32_t tau;        // the request's bound
@@ -984,12 +1005,14 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
   b.cnt = a.C;
   b.codes = nullptr;
   b.lprow = a.logprobs + (size_t)slot * a.C;
+  b.beg = 0;
   b.live = b.s != -INFINITY && !__builtin_isnan(b.s);
   if (__builtin_isnan(b.s)) fl |= GRW_FLAG_NAN_LOGPROB;
   if (b.live && !beam_row(a, slot, b.cnt, b.codes)) {
     fl |= GRW_FLAG_BAD_NODE;
     b.live = false;
   }
+  if (b.live && b.codes != nullptr) b.beg = (int)(b.codes - a.code);
   if (b.live && b.cnt > kOnePass) {              // longer than the code range: corrupt row
     fl |= GRW_FLAG_BAD_NODE;
     b.live = false;
@@ -1015,25 +1038,48 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
     asm volatile("" : "+v"(fb));
     return fb + (uint32_t)rr.code_of(k);
   };
-  uint32_t ok[kRegC];
+  // Admission in the float domain: for a non-NaN key, key >= tau_f exactly when its
+  // ordered key is >= tau (-0.0 and +0.0 compare equal on both sides); NaN keys and the -inf
+  // of positions without a candidate never pass.  Most rows admit a handful of candidates,
+  // so ordered keys are formed only for those.
+  const float tau_f = tau < 0x00800000u ? -3.402823466e+38f : float_of_ordered(tau);   // -FLT_MAX: every finite key
+  float kf[kRegC];
   int na = 0;
+  bool suspect = false;
 #pragma unroll
   for (int k = 0; k < kRegC; ++k) {
-    ok[k] = row_key<L>(rr, k, b.cnt, b.s, tau, fl);
-    na += ok[k] != 0u;
+    const float lp = rr.lp[k];
+    suspect |= !(lp <= 0.0f);                    // NaN or positive: a precondition flag
+    kf[k] = b.s + lp;
+    na += kf[k] >= tau_f;
   }
-  auto key = [&](int k) -> uint32_t { return ok[k]; };
+  if (suspect) {
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      if (__builtin_isnan(rr.lp[k])) fl |= GRW_FLAG_NAN_LOGPROB;
+      else if (rr.lp[k] > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
+    }
+  }
   int n;
   int p = block_excl_scan256(na, red, &n);      // offsets, valid while every candidate is kept
   if (n == 0) return 0;
   const int K = rd.K;
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
+  int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
   if (n <= K && n < rd.W) {
 #pragma unroll
-    for (int k = 0; k < kRegC; ++k)
-      if (ok[k]) st_dev(&region[p++], composite_key(ok[k], flat(k)));
+    for (int k = 0; k < kRegC; ++k) {
+      if (kf[k] >= tau_f) {
+        if constexpr (L == kTrie) st_dev(&redge[p], b.beg + (int)threadIdx.x + 256 * k);
+        st_dev(&region[p++], composite_key(ordered_key(kf[k]), flat(k)));
+      }
+    }
     return n;
   }
+  uint32_t ok[kRegC];
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) ok[k] = kf[k] >= tau_f ? ordered_key(kf[k]) : 0u;
+  auto key = [&](int k) -> uint32_t { return ok[k]; };
   uint64_t T = 1;
   int n_out = n;
   if (n > K) {
@@ -1053,8 +1099,12 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   int total;
   p = block_excl_scan256(__builtin_popcount(keep), red, &total);
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k)
-    if ((keep >> k) & 1u) st_dev(&region[p++], composite_key(ok[k], flat(k)));
+  for (int k = 0; k < kRegC; ++k) {
+    if ((keep >> k) & 1u) {
+      if constexpr (L == kTrie) st_dev(&redge[p], b.beg + (int)threadIdx.x + 256 * k);
+      st_dev(&region[p++], composite_key(ok[k], flat(k)));
+    }
+  }
   return min(total, K);     // the entries written (n_out by construction)
 }
 
@@ -1082,7 +1132,7 @@ __global__ __launch_bounds__(256) void select_fused_kernel(SelArgs a) {
   if (tid == 0) last_s = atomicAdd(&a.done_count[b.r], 1u) + 1u == (uint32_t)a.req[b.r].W;
   __syncthreads();
   if (!last_s) return;
-  final_select<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap>(a, b.r, fin);
+  final_select<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap>(a, b.r, fin);
   __syncthreads();
   if (tid == 0) {
     a.done_count[b.r] = 0u;
