@@ -478,6 +478,17 @@ def main():
     log(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms")
     decode_steps = wl.S * args.steps
     value = decode_steps / wall
+    # the same loop captured as one HIP graph and replayed (no host work between kernels)
+    graph = loop.capture(lps, layers, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_wall = time.perf_counter() - t0
+    del graph
+    graph_value = decode_steps / graph_wall
+    log(f"[bench] graph replay of {args.steps} steps: wall {graph_wall * 1e3:.2f} ms")
 
     if args.stage_reps > 0:
         stages = stage_timings(wl, st, args.stage_reps)
@@ -530,6 +541,7 @@ def main():
                    "decode_steps_per_bench_step": wl.S,
                    "trie": None if wl.catalog is None else f"{wl.catalog[0]} {wl.catalog[1]} items",
                    "device_flags": flags},
+        "graph_replay_value": round(graph_value, 2),
         "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
         "select_roofline": sel_roof,

@@ -56,6 +56,20 @@ class DecodeLoop:
         if steps == self.S:
             grw_backtrack(self.ws, self.tokens, self.parents, self.S, self.sid, stream)
 
+    def capture(self, logprobs, layers, out, steps=None):
+        """Record run() as one HIP graph (xLLM design doc, section 3.2, and the FlashRec
+        announcement: the decode steps as one captured graph, with no host work between
+        kernels).  Every kernel of the loop reads and writes preallocated buffers and the
+        library records no memset, so replaying the graph repeats run() exactly.  One eager
+        run first performs the library's one-time set-up outside the capture.  Returns the
+        torch.cuda.CUDAGraph; call .replay() on it."""
+        self.run(logprobs, layers, out, steps=steps)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(logprobs, layers, out, steps=steps)
+        return graph
+
     def final_scores(self):
         return self.scores[self.S % 2]
 
