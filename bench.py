@@ -252,7 +252,7 @@ def select_roofline(seed, dev, reps):
             "live_beams": live, "bytes_per_call": bytes_, "avg_call_us": round(t * 1e6, 2),
             "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
             "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
-            "kernels": "select_pilot_kernel + select_fused_kernel"}
+            "kernels": "select_pilot_kernel + select_beam_kernel + select_final_kernel"}
 
 
 # ----------------------------------------------------------------------------------------

@@ -38,7 +38,7 @@ struct grw_ws {
   int32_t* d_pilot_desc = nullptr;
   uint64_t* d_pilot_buf = nullptr;
   int32_t* d_order = nullptr;
-  uint32_t* d_step_state = nullptr;    // [3][max_requests]: pilot count, pilot ready, done count
+  uint32_t* d_step_state = nullptr;    // [max_requests]: pilots finished in the current step
   int32_t* d_flags = nullptr;
   // pinned host staging for the bind upload
   void* h_stage = nullptr;
@@ -260,7 +260,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 4 * B);
   if (st == GRW_OK) st = dev_alloc(&w->d_order, B);
-  if (st == GRW_OK) st = dev_alloc(&w->d_step_state, 3LL * L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_step_state, (int64_t)L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
   if (st == GRW_OK) {
@@ -273,7 +273,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   }
   if (st == GRW_OK) {
     if (hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
-        hipMemset(w->d_step_state, 0, sizeof(uint32_t) * 3 * L.max_requests) != hipSuccess ||
+        hipMemset(w->d_step_state, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
 
         hipMemset(w->d_flags, 0, sizeof(int32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
@@ -495,8 +495,6 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
   a.pilot_buf = w->d_pilot_buf;
   a.order = w->d_order;
   a.pilot_count = w->d_step_state;
-  a.pilot_ready = w->d_step_state + L.max_requests;
-  a.done_count = w->d_step_state + 2 * L.max_requests;
   a.out_token = out_token;
   a.out_parent = out_parent;
   a.out_score = out_score;

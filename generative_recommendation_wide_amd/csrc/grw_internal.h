@@ -91,9 +91,7 @@ struct SelArgs {
   int32_t n_pilots;
   uint64_t* pilot_buf;      // [R][kPilotCap] pilot candidates
   const int32_t* order;     // [sumW] beam slot of each fused-step workgroup (pilots first)
-  uint32_t* pilot_count;    // [R] pilots finished this step (fused step)
-  uint32_t* pilot_ready;    // [R] 1 once the pilot bound is published (fused step)
-  uint32_t* done_count;     // [R] workgroups finished this step (fused step)
+  uint32_t* pilot_count;    // [R] pilots finished this step
   int32_t* out_token;
   int32_t* out_parent;
   float* out_score;

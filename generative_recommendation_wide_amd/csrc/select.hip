@@ -137,6 +137,26 @@ __device__ __forceinline__ int block_excl_scan256(int v, int* red, int* total) {
   return before + incl - v;
 }
 
+// Exclusive prefix of v over the NT threads; *total receives the sum.  red holds NT / 64
+// entries.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int* total) {
+  constexpr int NW = NT / 64;
+  const int incl = wave_inclusive_scan(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) before += red[w];
+    all += red[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
 // Threshold T such that exactly N of the non-zero entries held by the threads are >= T
 // (1 <= N <= their count; NT threads, each holding NR entries get(0..NR-1), 0 = none).
 // Radix select as above, starting at the highest bit in which the entries differ.
@@ -972,17 +992,16 @@ __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) 
 }
 
 // --------------------------------------------------------------------------------------
-// per-beam top-k and the W-of-pool select in one kernel
+// register-resident step: per-beam stage, then the W-of-pool stage
 // --------------------------------------------------------------------------------------
 // Used when every row fits the one-read path (C <= kOnePass) and W <= kFusedMaxW, after
-// select_pilot has set the bounds.  One workgroup per beam slot; survivors and counts are
-// stored device-coherently, each slot counts itself done, and the workgroup that completes
-// a request runs its W-of-pool select and resets the request's step state.
+// select_pilot has set the bounds.  The per-beam kernel runs one small workgroup per beam
+// slot (few registers and no large LDS arrays, so every slot of a wide batch is resident
+// at once); the W-of-pool kernel runs one 1024-thread workgroup per request.
 constexpr int kFusedMaxW = 1024;
 constexpr int kFusedBins = 1024;
 constexpr int kFusedBinCap = 512;
 constexpr int kFusedWinCap = kFusedMaxW + kFusedBinCap;
-typedef FinalLds<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedWinCap> FusedLds;
 
 struct BeamRow {
   int slot, r, cnt;
@@ -1020,38 +1039,30 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
   return b;
 }
 
-// Survivors of one loaded beam row: candidates >= the request's bound, at most K of them
-// (radix select over the registers), stored device-coherently in the beam's pool region.
-// Publishes the beam's own W_r-th best when it alone holds >= W_r survivors.  Returns the
-// survivor count.  Reached by every thread of the workgroup.
+// Survivors of one loaded beam row: candidates >= the request's bound, stored in the beam's
+// pool region.  Returns the survivor count, or -1 when the row has more than top_k of them
+// (nothing is stored; the request's W-of-pool workgroup selects that row's top_k).  Reached
+// by every thread of the workgroup.
 template <int L>
-__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L>& rr, int& fl, uint32_t* hist,
-                         uint32_t* scr, uint32_t* red32, int* red) {
+__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L>& rr, int& fl, int* red) {
   const ReqDesc& rd = b.rd;
   const uint32_t tau = b.tau;
   // a beam below the bound keeps nothing: no key exceeds its beam's score
   if (!b.live || ordered_key(b.s) < tau) return 0;
   const int j = b.slot - rd.boff;
   const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
-  auto flat = [&](int k) -> uint32_t {
-    uint32_t fb = flat_base;
-    asm volatile("" : "+v"(fb));
-    return fb + (uint32_t)rr.code_of(k);
-  };
   // Admission in the float domain: for a non-NaN key, key >= tau_f exactly when its
   // ordered key is >= tau (-0.0 and +0.0 compare equal on both sides); NaN keys and the -inf
   // of positions without a candidate never pass.  Most rows admit a handful of candidates,
   // so ordered keys are formed only for those.
   const float tau_f = tau < 0x00800000u ? -3.402823466e+38f : float_of_ordered(tau);   // -FLT_MAX: every finite key
-  float kf[kRegC];
   int na = 0;
   bool suspect = false;
 #pragma unroll
   for (int k = 0; k < kRegC; ++k) {
     const float lp = rr.lp[k];
     suspect |= !(lp <= 0.0f);                    // NaN or positive: a precondition flag
-    kf[k] = b.s + lp;
-    na += kf[k] >= tau_f;
+    na += b.s + lp >= tau_f;
   }
   if (suspect) {
 #pragma unroll
@@ -1061,83 +1072,134 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
     }
   }
   int n;
-  int p = block_excl_scan256(na, red, &n);      // offsets, valid while every candidate is kept
+  int p = block_excl_scan<256>(na, red, &n);
   if (n == 0) return 0;
   const int K = rd.K;
+  if (n > K) return -1;
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
   int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
-  if (n <= K && n < rd.W) {
 #pragma unroll
-    for (int k = 0; k < kRegC; ++k) {
-      if (kf[k] >= tau_f) {
-        if constexpr (L == kTrie) st_dev(&redge[p], b.beg + (int)threadIdx.x + 256 * k);
-        st_dev(&region[p++], composite_key(ordered_key(kf[k]), flat(k)));
-      }
+  for (int k = 0; k < kRegC; ++k) {
+    const float kf = b.s + rr.lp[k];
+    if (kf >= tau_f) {
+      if constexpr (L == kTrie) redge[p] = b.beg + (int)threadIdx.x + 256 * k;
+      region[p++] = composite_key(ordered_key(kf), flat_base + (uint32_t)rr.code_of(k));
     }
-    return n;
   }
-  uint32_t ok[kRegC];
+  return n;
+}
+
+// The top_k survivors of an overflowing beam row (more than top_k candidates >= the bound),
+// by the NT threads of the request's W-of-pool workgroup: the row is read again, NR
+// positions per thread (rows of at most NT * NR candidates), a radix select finds the
+// top_k-th composite, and the survivors go to the beam's pool region.
+template <int NT, int NR>
+__device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd, int r, int slot, uint32_t* hist,
+                                             uint32_t* scr, uint32_t* red32, int* red) {
+  const int tid = threadIdx.x;
+  const int j = slot - rd.boff;
+  const float s = a.scores[slot];
+  int cnt = a.C;
+  const int32_t* codes = nullptr;
+  if (!beam_row(a, slot, cnt, codes) || cnt > NT * NR) {   // never for rows the beam stage admitted
+    if (tid == 0) st_dev(&a.surv_count[slot], 0);
+    return;
+  }
+  const uint32_t tau = ld_dev(&a.bound[r]);
+  const float tau_f = tau < 0x00800000u ? -3.402823466e+38f : float_of_ordered(tau);
+  const float* lprow = a.logprobs + (size_t)slot * a.C;
+  const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
+  const int beg = codes != nullptr ? (int)(codes - a.code) : 0;
+  float lp[NR];
+  int code[NR];
+  int na = 0;
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k) ok[k] = kf[k] >= tau_f ? ordered_key(kf[k]) : 0u;
-  auto key = [&](int k) -> uint32_t { return ok[k]; };
-  uint64_t T = 1;
-  int n_out = n;
-  if (n > K) {
-    T = regs_select_composite<256, kRegC>(key, flat, K, n, hist, scr, red32);
-    n_out = K;
+  for (int k = 0; k < NR; ++k) {
+    const int i = tid + NT * k;
+    code[k] = i < cnt ? (codes != nullptr ? codes[i] : i) : -1;
+    if ((unsigned)code[k] >= (unsigned)a.C) code[k] = -1;
+    lp[k] = code[k] >= 0 ? lprow[code[k]] : -INFINITY;
+    na += s + lp[k] >= tau_f;
   }
-  if (n_out >= rd.W) {                           // this beam alone bounds the request's W-th best
-    const uint64_t TW = (n_out == rd.W) ? T : regs_select_composite<256, kRegC>(key, flat, rd.W, n, hist, scr, red32);
-    if (threadIdx.x == 0) atomicMax(&a.bound[b.r], (uint32_t)(TW >> 32));
-  }
-  // survivors as a bit mask (keeps the 64-bit composites out of registers)
+  int n;
+  (void)block_excl_scan<NT>(na, red, &n);
+  const int K = rd.K;
+  auto key = [&](int k) -> uint32_t {
+    const float kf = s + lp[k];
+    return kf >= tau_f ? ordered_key(kf) : 0u;
+  };
+  auto flat = [&](int k) -> uint32_t { return flat_base + (uint32_t)code[k]; };
+  const uint64_t T = n > K ? regs_select_composite<NT, NR>(key, flat, K, n, hist, scr, red32) : 1ull;
   const uint32_t thi = (uint32_t)(T >> 32), tlo = (uint32_t)T;
   uint32_t keep = 0;
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k)
-    if (ok[k] > thi || (ok[k] == thi && ok[k] != 0u && ~flat(k) >= tlo)) keep |= 1u << k;
+  for (int k = 0; k < NR; ++k) {
+    const uint32_t ok = key(k);
+    if (ok > thi || (ok == thi && ok != 0u && ~flat(k) >= tlo)) keep |= 1u << k;
+  }
   int total;
-  p = block_excl_scan256(__builtin_popcount(keep), red, &total);
+  int p = block_excl_scan<NT>(__builtin_popcount(keep), red, &total);
+  uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
+  int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k) {
+  for (int k = 0; k < NR; ++k) {
     if ((keep >> k) & 1u) {
-      if constexpr (L == kTrie) st_dev(&redge[p], b.beg + (int)threadIdx.x + 256 * k);
-      st_dev(&region[p++], composite_key(ok[k], flat(k)));
+      if (codes != nullptr) st_dev(&redge[p], beg + tid + NT * k);
+      st_dev(&region[p++], composite_key(key(k), flat(k)));
     }
   }
-  return min(total, K);     // the entries written (n_out by construction)
+  if (tid == 0) st_dev(&a.surv_count[slot], min(total, K));
 }
 
+// Per-beam stage: survivors of each beam slot (candidates >= the request's bound) into the
+// slot's pool region, and the slot's survivor count (-1: more than top_k, left to the
+// W-of-pool stage).
 template <int L>
-__global__ __launch_bounds__(256) void select_fused_kernel(SelArgs a) {
-  __shared__ FusedLds fin;
-  __shared__ uint32_t red32[8];
+__global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   __shared__ int red[4];
-  __shared__ int last_s;
   const int tid = threadIdx.x;
   const int slot = blockIdx.x;
   int fl = 0;
   const BeamRow b = beam_setup(a, slot, fl);
   RowRegs<L> rr;
   if (b.live) load_row<L>(rr, a, b.lprow, b.codes, b.cnt, fl);
-  const int n_out = keep_beam<L>(a, b, rr, fl, fin.hist, fin.scr, red32, red);
-  if (tid == 0) st_dev(&a.surv_count[slot], n_out);
+  const int n_out = keep_beam<L>(a, b, rr, fl, red);
+  if (tid == 0) a.surv_count[slot] = n_out;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
   if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
+}
 
-  // ---- count the slot done; the workgroup completing its request selects the beams ----
+// W-of-pool stage: one workgroup of 1024 threads per request, after every beam's survivors
+// are in the pool; resets the request's bound for the next step.
+constexpr int kFinThreads = 1024;
+typedef FinalLds<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedWinCap> FinLds;
+
+__global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  FinLds& L = *(FinLds*)smem;
+  __shared__ int red[kFinThreads / 64];
+  __shared__ uint32_t red32[2 * (kFinThreads / 64)];
+  __shared__ int n_over;
+  const int r = blockIdx.x;
+  const ReqDesc rd = a.req[r];
+  // beams whose rows overflowed top_k: their survivors first (listed in L.pre meanwhile)
+  if (threadIdx.x == 0) n_over = 0;
+  __syncthreads();
+  for (int jj = threadIdx.x; jj < rd.W; jj += kFinThreads)
+    if (a.surv_count[rd.boff + jj] < 0) L.pre[atomicAdd(&n_over, 1)] = (uint32_t)(rd.boff + jj);
+  __syncthreads();
+  const int no = n_over;
+  for (int i = 0; i < no; ++i) {
+    const int slot = (int)L.pre[i];
+    __syncthreads();
+    overflow_row<kFinThreads, kOnePass / kFinThreads>(a, rd, r, slot, L.hist, L.scr, red32, red);
+  }
   wait_stores();
   __syncthreads();
-  if (tid == 0) last_s = atomicAdd(&a.done_count[b.r], 1u) + 1u == (uint32_t)a.req[b.r].W;
+  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap>(a, r, L);
   __syncthreads();
-  if (!last_s) return;
-  final_select<256, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap>(a, b.r, fin);
-  __syncthreads();
-  if (tid == 0) {
-    a.done_count[b.r] = 0u;
-    a.bound[b.r] = 0u;
-  }
+  if (threadIdx.x == 0) a.bound[r] = 0u;
 }
 
 __global__ void beams_init_kernel(const ReqDesc* req, const int32_t* slot_req, int sumW,
@@ -1201,14 +1263,22 @@ bool select_fused_ok(int C, int max_W) { return C <= kOnePass && max_W <= kFused
 
 hipError_t launch_select_fused(const SelArgs& a, hipStream_t s) {
   if (a.sumW == 0) return hipSuccess;
+  static bool attr_set = false;   // the W-of-pool select's arrays exceed the default 64 KB
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)select_final_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   select_pilot_kernel<<<a.n_pilots, 256, 0, s>>>(a);
   const int grid = a.sumW;
   if (a.row_ptr != nullptr)
-    select_fused_kernel<kTrie><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kTrie><<<grid, 256, 0, s>>>(a);
   else if ((a.C & 3) == 0 && (((uintptr_t)a.logprobs) & 15) == 0)
-    select_fused_kernel<kFull><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kFull><<<grid, 256, 0, s>>>(a);
   else
-    select_fused_kernel<kFullScalar><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kFullScalar><<<grid, 256, 0, s>>>(a);
+  select_final_kernel<<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
   return hipGetLastError();
 }
 
