@@ -6,7 +6,9 @@ Sources:
   pool; §4.3: invalid item paths are filtered during the search.
 * FlashRec announcement (SGLang PR thread): with the semantic-ID trie, illegal IDs are
   never candidates.
-* FlashRec deployment guide, request section: temperature 0 gives a deterministic top-k.
+* FlashRec deployment guide, request section: temperature 0 gives a deterministic top-k;
+  a positive temperature gives a Gumbel top-k whose noise only orders the candidates, the
+  returned sequence score holding none of it.
 
 Readings where the pages are silent (each is the plainest one the rest supports):
 * the ranking key of candidate (b, c) is the float32 sum score_b + lp[b, c] (one IEEE
@@ -18,7 +20,13 @@ Readings where the pages are silent (each is the plainest one the rest supports)
   pad slots (token -1, parent -1, score -inf) after all real slots;
 * at level 0 only slot 0 is live (score 0, empty prefix);
 * code c is valid for a beam with prefix p at level l iff p + (c,) is the length-(l+1)
-  prefix of some catalog item (decided from the raw item list).
+  prefix of some catalog item (decided from the raw item list);
+* Gumbel top-k at temperature T >= 0 with noise g (standard Gumbel draws, an input): the
+  ordering key of (b, c) is float32(key + float32(T * g[b, c])), two IEEE roundings;
+  every top_k / beam_width decision and tie rule above uses it in place of the key, and
+  the returned score is the key itself.  Multiplying the noise by T keeps the key's units;
+  for T > 0 the order equals that of key / T + g, the Gumbel-max form of sampling
+  proportionally to exp(key / T).  A candidate whose ordering key is -inf is dropped.
 """
 from __future__ import annotations
 
@@ -48,7 +56,7 @@ def _is_member(sorted_set: np.ndarray, keys: np.ndarray) -> np.ndarray:
     return (idx < sorted_set.size) & (sorted_set[idx_c] == keys)
 
 
-def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
+def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=None, temperature=0.0):
     """One selection step of one request.
 
     lp        float32 [Wslots][C]   log-probabilities of this step
@@ -57,6 +65,8 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
     level     number of codes already in each live prefix
     K, W      top_k and beam_width of the request
     prefix_sets  output of catalog_prefix_sets, or None when unconstrained
+    noise     float32 [Wslots][C] Gumbel draws of the sampled selection, or None
+    temperature  T >= 0 of the sampled selection (T = 0 orders by the key alone)
 
     Returns a dict: tokens int32 [W], parents int32 [W], scores float32 [W],
     prefixes (list of packed prefixes, None for pad slots) and pool_size (the number of
@@ -65,8 +75,13 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
     lp = np.asarray(lp, dtype=np.float32)
     scores = np.asarray(scores, dtype=np.float32)
     assert not np.isnan(scores).any()
+    t = np.float32(temperature)
+    assert np.isfinite(t) and t >= 0
+    if noise is not None:
+        noise = np.asarray(noise, dtype=np.float32)
+        assert np.isfinite(noise).all()
     all_codes = np.arange(C, dtype=np.int64)
-    pool_key, pool_flat = [], []
+    pool_key, pool_okey, pool_flat = [], [], []
     for b in range(scores.shape[0]):
         s = scores[b]
         if s == NEG_INF:
@@ -77,10 +92,13 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
         keys = s + lp[b, codes]                       # float32 + float32 -> float32
         assert keys.dtype == np.float32
         assert not np.isnan(keys).any(), "NaN log-probability"
-        live = keys != NEG_INF
-        codes, keys = codes[live], keys[live]
-        order = np.lexsort((codes, -keys))[:K]        # full stable sort, keep top_k
+        okeys = keys if noise is None else keys + t * noise[b, codes]   # two float32 roundings
+        assert okeys.dtype == np.float32
+        live = (keys != NEG_INF) & (okeys != NEG_INF)
+        codes, keys, okeys = codes[live], keys[live], okeys[live]
+        order = np.lexsort((codes, -okeys))[:K]       # full stable sort, keep top_k
         pool_key.append(keys[order])
+        pool_okey.append(okeys[order])
         pool_flat.append(b * C + codes[order])
     tokens = np.full(W, -1, np.int32)
     parents = np.full(W, -1, np.int32)
@@ -88,8 +106,9 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None):
     new_prefixes = [None] * W
     if pool_key:
         key = np.concatenate(pool_key)
+        okey = np.concatenate(pool_okey)
         flat = np.concatenate(pool_flat)
-        order = np.lexsort((flat, -key))[:W]
+        order = np.lexsort((flat, -okey))[:W]
         n = order.size
         tokens[:n] = flat[order] % C
         parents[:n] = flat[order] // C
@@ -110,15 +129,17 @@ def initial_beams(W):
     return scores, prefixes
 
 
-def oracle_beam_search(lp_of_step, W, K, C, S, prefix_sets=None):
-    """S selection steps of one request.  ``lp_of_step(d)`` returns float32 [W][C].
+def oracle_beam_search(lp_of_step, W, K, C, S, prefix_sets=None, noise_of_step=None, temperature=0.0):
+    """S selection steps of one request.  ``lp_of_step(d)`` returns float32 [W][C], and
+    ``noise_of_step(d)`` the step's Gumbel draws for the sampled selection.
 
     Returns the list of per-step results of oracle_select.
     """
     scores, prefixes = initial_beams(W)
     steps = []
     for d in range(S):
-        res = oracle_select(lp_of_step(d), scores, prefixes, d, K, W, C, prefix_sets)
+        noise = noise_of_step(d) if noise_of_step is not None else None
+        res = oracle_select(lp_of_step(d), scores, prefixes, d, K, W, C, prefix_sets, noise, temperature)
         steps.append(res)
         scores, prefixes = res["scores"], res["prefixes"]
     return steps

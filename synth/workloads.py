@@ -20,7 +20,7 @@ from typing import Optional
 import numpy as np
 
 # stream ids (fixed order, part of the recipe)
-_S_CATALOG, _S_SHAPES, _S_Q, _S_KS, _S_VS, _S_KU, _S_VU, _S_LOGITS, _S_PARENTS = range(9)
+_S_CATALOG, _S_SHAPES, _S_Q, _S_KS, _S_VS, _S_KU, _S_VU, _S_LOGITS, _S_PARENTS, _S_GUMBEL = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -365,3 +365,24 @@ def logprob_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None)
     if rows is not None:
         lp = lp[np.asarray(rows)]
     return lp
+
+
+def gumbel_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None):
+    """Standard Gumbel draws [sumW][C] float32 for the sampled selection of one step.
+
+    u is uniform on the open interval (0, 1) at 53-bit resolution ((k + 1/2) / 2^53 for an
+    integer k), g = -log(-log(u)) in float64, rounded once to float32; every value is
+    finite (about -3.6 .. 37.4).  The selection draws no random numbers itself: these
+    rows are its noise input.  ``rows`` optionally selects a subset of slot rows.
+    """
+    if wl.name == "ultra5000":
+        raise NotImplementedError("noise rows are not generated for the ultra-wide workload")
+    W, K, P = shapes if shapes is not None else request_shapes(wl, seed)
+    sumW = int(W.sum())
+    g = _rng(seed, wl, _S_GUMBEL, step)
+    k = g.integers(0, 1 << 53, size=(sumW, wl.C), dtype=np.int64)
+    u = (k.astype(np.float64) + 0.5) / float(1 << 53)
+    out = (-np.log(-np.log(u))).astype(np.float32)
+    if rows is not None:
+        out = out[np.asarray(rows)]
+    return out

@@ -9,6 +9,12 @@ S4  with prefix-keyed log-probabilities and W >= |catalog|, the beam set after L
     the whole catalog, ordered by the recursively defined tie rule;
 S5  invariants on the synthetic workloads;
 and the candidate-pool size the design doc prints for beam_width = top_k = 512.
+
+Gumbel top-k (temperature T, noise g): G1 the enumeration above with perturbed ordering keys
+float32(key + float32(T * g)); G2 T = 0 reduces exactly to the deterministic selection; G3
+the Gumbel-max law: with one live beam and W = K = 1 the selected code is distributed as
+softmax(lp / T) (chi-square over 20 000 draws); G4 the returned scores hold no noise and the
+outputs are ordered by the perturbed key.
 """
 import os
 import struct
@@ -27,8 +33,11 @@ def f32(x: float) -> float:
     return struct.unpack("<f", struct.pack("<f", x))[0]
 
 
-def enumerate_select(lp, scores, prefixes, level, K, W, C, items):
-    """Independent pure-Python selection by enumeration of the whole W x C grid."""
+def enumerate_select(lp, scores, prefixes, level, K, W, C, items, noise=None, temperature=0.0):
+    """Independent pure-Python selection by enumeration of the whole W x C grid.  With
+    noise, candidates are ordered by float32(key + float32(T * g)) and keep their key as
+    score.  (Each float32 operation is done in double and rounded once: for a sum or
+    product of two float32 values that equals the float32 operation.)"""
     L = len(items[0]) if items else 0
     prefix_set = {tuple(it[:level + 1]) for it in items} if items is not None else None
     cands = []
@@ -41,7 +50,12 @@ def enumerate_select(lp, scores, prefixes, level, K, W, C, items):
             key = f32(float(s) + float(lp[b][c]))         # fp32 + fp32, rounded once
             if key == NEG_INF:
                 continue
-            cands.append((key, b, c))
+            okey = key
+            if noise is not None:
+                okey = f32(key + f32(f32(temperature) * float(noise[b][c])))
+                if okey == NEG_INF:
+                    continue
+            cands.append((okey, b, c, key))
     # per-beam top-K membership: fewer than K candidates of the same beam rank above it
     def better(x, y):   # x ranks strictly above y
         return x[0] > y[0] or (x[0] == y[0] and x[1] * C + x[2] < y[1] * C + y[2])
@@ -50,7 +64,7 @@ def enumerate_select(lp, scores, prefixes, level, K, W, C, items):
     sel = pool[:W]
     tokens = [x[2] for x in sel] + [-1] * (W - len(sel))
     parents = [x[1] for x in sel] + [-1] * (W - len(sel))
-    sc = [x[0] for x in sel] + [NEG_INF] * (W - len(sel))
+    sc = [x[3] for x in sel] + [NEG_INF] * (W - len(sel))
     newp = [tuple(prefixes[x[1]]) + (x[2],) for x in sel] + [None] * (W - len(sel))
     return tokens, parents, sc, newp, len(pool)
 
@@ -63,7 +77,7 @@ def _unpack(p, C, L):
     return tuple(reversed(out))
 
 
-def _run_both(rng, W, K, C, L, n_items, tie_values, steps=None):
+def _run_both(rng, W, K, C, L, n_items, tie_values, steps=None, sampled=False):
     items = None
     if n_items:
         space = C ** L
@@ -78,8 +92,16 @@ def _run_both(rng, W, K, C, L, n_items, tie_values, steps=None):
             lp = rng.choice(np.array([0.0, -0.0, -0.5, -1.0, -np.inf], np.float32), size=(W, C))
         else:
             lp = np.minimum(rng.standard_normal((W, C)).astype(np.float32), 0)
-        res = oracle_select(lp, scores, prefixes, level, K, W, C, psets)
-        t2, p2, s2, np2, pool2 = enumerate_select(lp.tolist(), scores.tolist(), tprefixes, level, K, W, C, items)
+        noise, temp = None, 0.0
+        if sampled:
+            temp = float(rng.choice([0.0, 0.25, 1.0, 3.0]))
+            if tie_values:      # few distinct values, so perturbed keys tie often
+                noise = rng.choice(np.array([0.0, -0.0, 0.5, -1.0, 2.0], np.float32), size=(W, C))
+            else:
+                noise = (-np.log(-np.log(rng.uniform(1e-12, 1.0, size=(W, C))))).astype(np.float32)
+        res = oracle_select(lp, scores, prefixes, level, K, W, C, psets, noise, temp)
+        t2, p2, s2, np2, pool2 = enumerate_select(lp.tolist(), scores.tolist(), tprefixes, level, K, W, C, items,
+                                                  noise.tolist() if noise is not None else None, temp)
         assert res["tokens"].tolist() == t2
         assert res["parents"].tolist() == p2
         assert [struct.pack("<f", x) for x in res["scores"].tolist()] == \
@@ -279,3 +301,83 @@ def test_csr_trie_agrees_with_catalog_prefixes():
         assert np.all(np.diff(code[rp[n]:rp[n + 1]]) > 0)
     for l in range(1, L + 1):
         assert np.array_equal(np.sort(t["node_prefix"][t["node_depth"] == l]), psets[l])
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_gumbel_exhaustive_enumeration_tiny_random(seed):
+    """G1: the sampled selection against the enumeration with perturbed ordering keys."""
+    rng = np.random.default_rng(300 + seed)
+    n_cases = int(os.environ.get("GRW_G1_CASES", "1500"))
+    for _ in range(n_cases):
+        W = int(rng.integers(1, 9))
+        K = int(rng.integers(1, 9))
+        C = int(rng.integers(2, 17))
+        L = int(rng.integers(1, 5))
+        n_items = int(rng.integers(0, 41))
+        _run_both(rng, W, K, C, L, n_items, tie_values=bool(rng.integers(0, 2)), sampled=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen06b"])
+def test_gumbel_temperature_zero_is_deterministic(name):
+    """G2: T = 0 gives exactly the deterministic selection, whatever the noise."""
+    from synth import gumbel_rows, request_shapes
+    wl = workload(name)
+    W, K, P = request_shapes(wl)
+    items = catalog_items(wl)
+    psets = catalog_prefix_sets(items, wl.C)
+    w, k = int(W[0]), int(K[0])
+    a = oracle_beam_search(lambda d: logprob_rows(wl, d)[:w], w, k, wl.C, wl.S, psets)
+    b = oracle_beam_search(lambda d: logprob_rows(wl, d)[:w], w, k, wl.C, wl.S, psets,
+                           noise_of_step=lambda d: gumbel_rows(wl, d)[:w], temperature=0.0)
+    for ra, rb in zip(a, b):
+        assert ra["tokens"].tolist() == rb["tokens"].tolist()
+        assert ra["parents"].tolist() == rb["parents"].tolist()
+        assert ra["scores"].view(np.uint32).tolist() == rb["scores"].view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("temp", [0.5, 1.0, 2.0])
+def test_gumbel_max_law(temp):
+    """G3: one live beam, W = K = 1, unconstrained: the chosen code follows softmax(lp / T)."""
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(7)
+    C, n = 6, 20000
+    logits = np.array([1.5, 0.2, -0.3, 0.9, -1.2, 0.0])
+    lp = (logits - np.log(np.exp(logits).sum())).astype(np.float32)[None, :]
+    scores, prefixes = initial_beams(1)
+    counts = np.zeros(C)
+    for _ in range(n):
+        g = (-np.log(-np.log(rng.uniform(1e-15, 1.0, size=(1, C))))).astype(np.float32)
+        res = oracle_select(lp, scores, prefixes, 0, 1, 1, C, None, g, temp)
+        counts[res["tokens"][0]] += 1
+    p = np.exp(lp[0].astype(np.float64) / temp)
+    p /= p.sum()
+    assert chisquare(counts, n * p).pvalue > 1e-4
+    # noise added without the temperature would give another law
+    q = np.exp(lp[0].astype(np.float64))
+    q /= q.sum()
+    if temp != 1.0:
+        assert chisquare(counts, n * q).pvalue < 1e-6
+
+
+def test_gumbel_scores_exclude_noise_and_order_by_perturbed_key():
+    """G4 on the qwen06b-shaped workload (one request, all steps, T = 1)."""
+    from synth import gumbel_rows, request_shapes
+    wl = workload("qwen06b")
+    W, K, P = request_shapes(wl)
+    items = catalog_items(wl)
+    psets = catalog_prefix_sets(items, wl.C)
+    w, k = int(W[0]), int(K[0])
+    scores, prefixes = initial_beams(w)
+    for d in range(wl.S):
+        lp = logprob_rows(wl, d)[:w]
+        g = gumbel_rows(wl, d)[:w]
+        res = oracle_select(lp, scores, prefixes, d, k, w, wl.C, psets, g, 1.0)
+        n = int((res["parents"] >= 0).sum())
+        par, tok = res["parents"][:n], res["tokens"][:n]
+        want = scores[par] + lp[par, tok]
+        assert res["scores"][:n].view(np.uint32).tolist() == want.view(np.uint32).tolist()
+        okey = want + np.float32(1.0) * g[par, tok]
+        flat = par.astype(np.int64) * wl.C + tok
+        assert all((okey[i] > okey[i + 1]) or (okey[i] == okey[i + 1] and flat[i] < flat[i + 1])
+                   for i in range(n - 1))
+        scores, prefixes = res["scores"], res["prefixes"]
