@@ -185,11 +185,13 @@ def stage_timings(wl, st, reps):
     return res
 
 
-def select_roofline(seed, dev, reps):
+def select_roofline(seed, dev, reps, temperature=None):
     """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
     262144-entry pools): device time of one call with every beam live (the third decode step,
     beams from two real selections), against the HBM time of its algorithmic bytes: every
-    beam's log-probability row, the beam scores, and the four output arrays."""
+    beam's log-probability row, the beam scores, and the four output arrays.  With a
+    temperature, beam_select_gumbel with standard Gumbel noise rows (one more row per beam
+    in the algorithmic bytes)."""
     import torch
 
     import generative_recommendation_wide_amd as grw
@@ -203,14 +205,20 @@ def select_roofline(seed, dev, reps):
         x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
         lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
         del x
+    noise = [None] * 3
+    if temperature is not None:
+        for i in range(3):
+            u = torch.rand(sumW, C, generator=g, device=dev, dtype=torch.float64).clamp_(1e-300, 1.0 - 1e-16)
+            noise[i] = (-torch.log(-torch.log(u))).to(torch.float32)
+            del u
     ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
                        max_C=C, max_S=wl.S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                        q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
     ws.bind_batch(W, K, P)
     loop = grw.DecodeLoop(ws, wl.S, C, None, device=dev)
     ws.beams_init(loop.scores[0], loop.nodes[0])
-    loop.select_step(0, lps[0])
-    loop.select_step(1, lps[1])
+    loop.select_step(0, lps[0], noise=noise[0], temperature=temperature or 0.0)
+    loop.select_step(1, lps[1], noise=noise[1], temperature=temperature or 0.0)
     sc, nd = loop.scores[0].clone(), loop.nodes[0].clone()     # step-2 input beams
     live = int((sc > float("-inf")).sum())
     tok, par = torch.empty(sumW, dtype=torch.int32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
@@ -219,7 +227,11 @@ def select_roofline(seed, dev, reps):
     Wm, Km = int(W.max()), int(K.max())
 
     def fn():
-        grw.beam_select(ws, lps[2], sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+        if temperature is None:
+            grw.beam_select(ws, lps[2], sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+        else:
+            grw.beam_select_gumbel(ws, lps[2], noise[2], temperature, sc, nd, None, None, 0, Wm, Km, C, tok, par,
+                                   osc, ond)
     ms_eager = time_stage(fn, reps, stream)
     ref = (tok.clone(), par.clone(), osc.clone())
     tok.fill_(-7)
@@ -243,7 +255,7 @@ def select_roofline(seed, dev, reps):
     same = bool(torch.equal(tok, ref[0]) and torch.equal(par, ref[1]) and
                 torch.equal(osc.view(torch.int32), ref[2].view(torch.int32)))
     pools = [ws.pool_size(r) for r in range(len(W))]
-    bytes_ = sumW * C * 4.0 + sumW * 4.0 + sumW * 16.0
+    bytes_ = sumW * C * 4.0 * (1 if temperature is None else 2) + sumW * 4.0 + sumW * 16.0
     t = ms / 1e3
     achieved = bytes_ / t / 1e9
     ws.close()
@@ -252,7 +264,8 @@ def select_roofline(seed, dev, reps):
             "live_beams": live, "bytes_per_call": bytes_, "avg_call_us": round(t * 1e6, 2),
             "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
             "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
-            "kernels": "select_pilot_kernel + select_beam_kernel + select_final_kernel"}
+            "kernels": "select_pilot_kernel + select_beam_kernel + select_final_kernel",
+            "entry_point": "beam_select" if temperature is None else f"beam_select_gumbel (temperature {temperature})"}
 
 
 # ----------------------------------------------------------------------------------------
@@ -428,6 +441,8 @@ def main():
                     help="also run one device copy of this size (counter calibration)")
     ap.add_argument("--select-only", action="store_true",
                     help="only the beam_select measurement on the unconstrained wide pool (for kernel traces)")
+    ap.add_argument("--select-temperature", type=float, default=None,
+                    help="with --select-only: time beam_select_gumbel at this temperature")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -453,7 +468,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.select_only:
-        print(json.dumps(select_roofline(args.seed, dev, 20)), flush=True)
+        print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature)), flush=True)
         return 0
     log(f"[bench] setting up {wl.name} ...")
     t_setup = time.perf_counter()
@@ -505,10 +520,12 @@ def main():
                 "kernel": DOMINANT, "flops_per_launch": flops, "avg_launch_us": round(t_shared * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_,
                 "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1)}
-    sel_roof = None
+    sel_roof = sel_gumbel = None
     if args.stage_reps > 0:
         sel_roof = select_roofline(args.seed, dev, 20 * args.stage_reps)
         log(f"[bench] select on wide512u: {sel_roof}")
+        sel_gumbel = select_roofline(args.seed, dev, 20 * args.stage_reps, temperature=1.0)
+        log(f"[bench] Gumbel select on wide512u: {sel_gumbel}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -545,6 +562,7 @@ def main():
         "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
         "select_roofline": sel_roof,
+        "select_gumbel_roofline": sel_gumbel,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -14,7 +14,8 @@ import torch
 from . import _lib
 from ._lib import (STAGE_MERGE, STAGE_SHARED, STAGE_UNSHARED,  # noqa: F401
                    FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING, FLAG_NAN_LOGPROB,  # noqa: F401
-                   FLAG_POS_LOGPROB, GRW_BF16, GRW_F32, GRW_FP8_E4M3, GrwError, GrwLimits)
+                   FLAG_BAD_NOISE, FLAG_POS_LOGPROB, GRW_BF16, GRW_F32, GRW_FP8_E4M3, GrwError,
+                   GrwLimits)
 
 _L = _lib.load()
 
@@ -130,6 +131,18 @@ def beam_select(ws: Workspace, logprobs, beam_scores, beam_node, trie_row_ptr, t
         _ptr(beam_node, _I32, "beam_node"), _ptr(trie_row_ptr, _I32, "trie_row_ptr"),
         _ptr(trie_code, _I32, "trie_code"), int(trie_n_internal), int(W), int(K), int(C),
         _ptr(out_token, _I32, "out_token"), _ptr(out_parent, _I32, "out_parent"),
+        _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
+
+
+def beam_select_gumbel(ws: Workspace, logprobs, noise, temperature: float, beam_scores, beam_node,
+                       trie_row_ptr, trie_code, trie_n_internal: int, W: int, K: int, C: int,
+                       out_token, out_parent, out_score, out_node, stream=None):
+    """The sampled selection step: Gumbel top-k at temperature >= 0 (see include/grw.h)."""
+    _lib.check("beam_select_gumbel", _L.beam_select_gumbel(
+        ws.handle, _ptr(logprobs, _F32, "logprobs"), _ptr(noise, _F32, "noise"), float(temperature),
+        _ptr(beam_scores, _F32, "beam_scores"), _ptr(beam_node, _I32, "beam_node"),
+        _ptr(trie_row_ptr, _I32, "trie_row_ptr"), _ptr(trie_code, _I32, "trie_code"), int(trie_n_internal),
+        int(W), int(K), int(C), _ptr(out_token, _I32, "out_token"), _ptr(out_parent, _I32, "out_parent"),
         _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
 
 

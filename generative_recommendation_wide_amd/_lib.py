@@ -16,10 +16,11 @@ GRW_OK, GRW_EINVAL, GRW_ENOMEM, GRW_EDEVICE, GRW_EUNSUPPORTED, GRW_ESTATE = rang
 GRW_F32, GRW_BF16, GRW_FP8_E4M3 = 0, 1, 2
 FLAG_NAN_LOGPROB, FLAG_POS_LOGPROB, FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_MISSING = 1, 2, 4, 8, 16
 FLAG_POOL_CORRUPT = 32
+FLAG_BAD_NOISE = 64
 STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
-            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
+            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "beam_select_gumbel", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
             "grw_ws_pool_size", "grw_status_str"]
 
 
@@ -56,6 +57,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "beam_attn_decode": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, vp],
         "beam_attn_decode_stages": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, i32, vp],
         "beam_select": [vp, fp, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp, i32p, vp],
+        "beam_select_gumbel": [vp, fp, fp, ctypes.c_float, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp,
+                               i32p, vp],
         "grw_backtrack": [vp, i32p, i32p, i32, i32p, vp],
         "grw_ws_error": [vp, vp, ctypes.POINTER(i32)],
         "grw_ws_splits": [vp, i32, ctypes.POINTER(i32)],

@@ -37,7 +37,6 @@ struct grw_ws {
   uint32_t* d_bound = nullptr;
   int32_t* d_pilot_desc = nullptr;
   uint64_t* d_pilot_buf = nullptr;
-  int32_t* d_order = nullptr;
   uint32_t* d_step_state = nullptr;    // [max_requests]: pilots finished in the current step
   int32_t* d_flags = nullptr;
   // pinned host staging for the bind upload
@@ -50,7 +49,8 @@ struct grw_ws {
   int maxW = 0, maxK = 0;
   int n_work = 0;
   int n_wide = 0;                // leading items of the work list that use the 8-wave kernel
-  int n_pilots = 0;              // pilot workgroups of the selection
+  int n_pilots = 0;              // pilot workgroups of the deterministic selection
+  int n_pilots_s = 0;            // pilot workgroups of the sampled selection
   std::vector<ReqDesc> req;
 };
 
@@ -90,7 +90,6 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_surv_count);
   (void)hipFree(w->d_bound);
   (void)hipFree(w->d_pilot_desc);
-  (void)hipFree(w->d_order);
   (void)hipFree(w->d_step_state);
   (void)hipFree(w->d_pilot_buf);
   (void)hipFree(w->d_flags);
@@ -161,16 +160,25 @@ void build_mfma_work(grw_ws* w, std::vector<ShWork>& out, int& n_wide) {
 }
 
 // Pilot beams of the selection: each pilot contributes one candidate per group of
-// pilot_g threads (a power of two; 256 / pilot_g <= top_k, so the contributions of one beam
-// never outnumber its pool entries).  Enough pilots for about 8 W candidates, at most
-// kMaxPilots beams and kPilotCap candidates per request.
-void set_pilots(ReqDesc& d, int32_t& pilot_off) {
-  int per = 1;
-  while (per * 2 <= std::min(d.K, 256)) per *= 2;
-  d.pilot_g = 256 / per;
+// 256 / per threads (per a power of two <= top_k, so the contributions of one beam never
+// outnumber its pool entries).  Enough pilots for about 8 W candidates, at most kMaxPilots
+// beams and kPilotCap candidates per request.  per is at most 256 for the deterministic
+// selection, whose slots are ordered by score so that the first beams hold most of the best
+// candidates, and at most 64 for the sampled one: there noise decides the slot order, and
+// contributions spread over more beams bound the W-th best key far more tightly (kept pool
+// 24 K -> 6.8 K entries on the W = K = 512 workload at temperature 1).
+int pilot_count(const ReqDesc& d, int max_per, int& per) {
+  per = 1;
+  while (per * 2 <= std::min(d.K, max_per)) per *= 2;
   const int64_t want = ceil_div(8LL * d.W, per);
-  int J = (int)std::min<int64_t>({(int64_t)d.W, (int64_t)kMaxPilots, (int64_t)(kPilotCap / per), want});
-  d.n_pilot = std::max(1, J);
+  const int J = (int)std::min<int64_t>({(int64_t)d.W, (int64_t)kMaxPilots, (int64_t)(kPilotCap / per), want});
+  return std::max(1, J);
+}
+
+void set_pilots(ReqDesc& d, int32_t& pilot_off) {
+  int per;
+  d.n_pilot = pilot_count(d, 256, per);
+  d.n_pilot_s = pilot_count(d, 64, per);
   d.pilot_off = pilot_off;
   pilot_off += kPilotCap;
 }
@@ -258,14 +266,13 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_pool_edge, w->pool_cap);
   if (st == GRW_OK) st = dev_alloc(&w->d_surv_count, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
-  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 4 * B);
-  if (st == GRW_OK) st = dev_alloc(&w->d_order, B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 8 * B);
   if (st == GRW_OK) st = dev_alloc(&w->d_step_state, (int64_t)L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
   if (st == GRW_OK) {
     w->stage_bytes = sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * B + sizeof(ShWork) * items +
-                     sizeof(int32_t) * 5 * B;
+                     sizeof(int32_t) * 8 * B;
     if (hipHostMalloc(&w->h_stage, w->stage_bytes, hipHostMallocDefault) != hipSuccess) {
       w->h_stage = nullptr;
       st = GRW_ENOMEM;
@@ -274,7 +281,6 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) {
     if (hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
         hipMemset(w->d_step_state, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
-
         hipMemset(w->d_flags, 0, sizeof(int32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
       st = GRW_EDEVICE;
@@ -342,24 +348,25 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   ShWork* hwork = (ShWork*)(h + sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * L.max_total_beams);
   int32_t* hpilot = (int32_t*)(hwork + w->work_cap);
   std::memcpy(hreq, w->req.data(), sizeof(ReqDesc) * n_requests);
-  int32_t* horder = hpilot + 4 * L.max_total_beams;
-  int n_pilots = 0;
-  for (int r = 0; r < n_requests; ++r) {
+  // pilot descriptors {slot, request, first pilot-buffer entry, threads per group}: the
+  // deterministic selection's, then the sampled selection's
+  int n_pilots = 0, n_pilots_s = 0;
+  for (int r = 0; r < n_requests; ++r)
     for (int b = 0; b < req[r].W; ++b) hslot[req[r].boff + b] = r;
-    const int per = 256 / req[r].pilot_g;
-    for (int j = 0; j < req[r].n_pilot; ++j, ++n_pilots) {
-      hpilot[4 * n_pilots + 0] = req[r].boff + j;
-      hpilot[4 * n_pilots + 1] = r;
-      hpilot[4 * n_pilots + 2] = req[r].pilot_off + j * per;
-      hpilot[4 * n_pilots + 3] = req[r].pilot_g;
+  for (int v = 0; v < 2; ++v) {
+    int32_t* hp = hpilot + (v == 0 ? 0 : 4 * n_pilots);
+    int n = 0;
+    for (int r = 0; r < n_requests; ++r) {
+      int per;
+      const int J = pilot_count(req[r], v == 0 ? 256 : 64, per);
+      for (int j = 0; j < J; ++j, ++n) {
+        hp[4 * n + 0] = req[r].boff + j;
+        hp[4 * n + 1] = r;
+        hp[4 * n + 2] = req[r].pilot_off + j * per;
+        hp[4 * n + 3] = 256 / per;
+      }
     }
-  }
-  // fused-step workgroup order: every request's pilot slots, then the remaining slots
-  for (int p = 0; p < n_pilots; ++p) horder[p] = hpilot[4 * p];
-  {
-    int o = n_pilots;
-    for (int r = 0; r < n_requests; ++r)
-      for (int b = req[r].n_pilot; b < req[r].W; ++b) horder[o++] = req[r].boff + b;
+    (v == 0 ? n_pilots : n_pilots_s) = n;
   }
   std::memcpy(hwork, work.data(), sizeof(ShWork) * work.size());
   hipStream_t s = (hipStream_t)stream;
@@ -368,9 +375,8 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   if (e == hipSuccess && !work.empty())
     e = hipMemcpyAsync(w->d_work, hwork, sizeof(ShWork) * work.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(w->d_pilot_desc, hpilot, sizeof(int32_t) * 4 * n_pilots, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(w->d_order, horder, sizeof(int32_t) * sumW, hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(w->d_pilot_desc, hpilot, sizeof(int32_t) * 4 * (n_pilots + n_pilots_s),
+                       hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     w->bound = false;
@@ -379,6 +385,7 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   w->n_work = (int)work.size();
   w->n_wide = n_wide;
   w->n_pilots = n_pilots;
+  w->n_pilots_s = n_pilots_s;
   w->maxW = maxW;
   w->maxK = maxK;
   w->bound = true;
@@ -458,10 +465,13 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
   return hip_status(e);
 }
 
-int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, const int32_t* beam_node,
-                const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
-                int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
-                float* out_score, int32_t* out_node, void* stream) {
+namespace {
+
+// One selection step, deterministic (noise == NULL) or Gumbel-sampled.
+int select_step(grw_ws* w, const float* logprobs, const float* noise, float temperature,
+                const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
+                const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
+                int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream) {
   if (!w) return GRW_EINVAL;
   if (!w->bound) return GRW_ESTATE;
   const grw_limits& L = w->lim;
@@ -478,6 +488,8 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
   a.req = w->d_req;
   a.slot_req = w->d_slot_req;
   a.logprobs = logprobs;
+  a.noise = noise;
+  a.temp = noise != nullptr ? temperature : 0.0f;
   a.scores = beam_scores;
   a.nodes = beam_node;
   a.row_ptr = trie ? trie_row_ptr : nullptr;
@@ -490,10 +502,9 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
   a.surv_count = w->d_surv_count;
   a.pool_edge = w->d_pool_edge;
   a.bound = w->d_bound;
-  a.pilot_desc = w->d_pilot_desc;
-  a.n_pilots = w->n_pilots;
+  a.pilot_desc = w->d_pilot_desc + (noise != nullptr ? 4 * w->n_pilots : 0);
+  a.n_pilots = noise != nullptr ? w->n_pilots_s : w->n_pilots;
   a.pilot_buf = w->d_pilot_buf;
-  a.order = w->d_order;
   a.pilot_count = w->d_step_state;
   a.out_token = out_token;
   a.out_parent = out_parent;
@@ -509,6 +520,26 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
     if (e == hipSuccess) e = launch_select_global(a, s);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, const int32_t* beam_node,
+                const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
+                int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
+                float* out_score, int32_t* out_node, void* stream) {
+  return select_step(w, logprobs, nullptr, 0.0f, beam_scores, beam_node, trie_row_ptr, trie_code,
+                     trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
+}
+
+int beam_select_gumbel(grw_ws* w, const float* logprobs, const float* noise, float temperature,
+                       const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
+                       const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K,
+                       int32_t C, int32_t* out_token, int32_t* out_parent, float* out_score,
+                       int32_t* out_node, void* stream) {
+  if (!noise || !(temperature >= 0.0f) || !std::isfinite(temperature)) return GRW_EINVAL;
+  return select_step(w, logprobs, noise, temperature, beam_scores, beam_node, trie_row_ptr, trie_code,
+                     trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
 }
 
 int grw_backtrack(grw_ws* w, const int32_t* tokens, const int32_t* parents, int32_t S,

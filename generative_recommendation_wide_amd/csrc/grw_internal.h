@@ -17,7 +17,7 @@ struct ReqDesc {
   int64_t kv_off;    // element offset of the request's prompt block in k_shared / v_shared
   int64_t pool_off;  // first candidate-pool entry of the request (W * min(K, C_max) entries)
   int32_t n_pilot;   // pilot beams of the selection (slots boff .. boff + n_pilot - 1)
-  int32_t pilot_g;   // threads per pilot group (one candidate per group; 256 / pilot_g <= K)
+  int32_t n_pilot_s; // pilot beams of the sampled (Gumbel) selection
   int32_t pilot_off; // first pilot-buffer entry of the request
   int32_t pad_;
 };
@@ -75,6 +75,8 @@ struct SelArgs {
   const ReqDesc* req;
   const int32_t* slot_req;
   const float* logprobs;
+  const float* noise;       // [sumW][C] Gumbel draws of the sampled selection, or NULL
+  float temp;               // its temperature (>= 0)
   const float* scores;
   const int32_t* nodes;
   const int32_t* row_ptr;   // NULL: unconstrained
@@ -90,7 +92,6 @@ struct SelArgs {
                                // threads per group, of each pilot workgroup
   int32_t n_pilots;
   uint64_t* pilot_buf;      // [R][kPilotCap] pilot candidates
-  const int32_t* order;     // [sumW] beam slot of each fused-step workgroup (pilots first)
   uint32_t* pilot_count;    // [R] pilots finished this step
   int32_t* out_token;
   int32_t* out_parent;

@@ -322,13 +322,33 @@ __device__ __forceinline__ bool beam_row(const SelArgs& a, int slot, int& cnt, c
   return true;
 }
 
+// Gumbel top-k (FlashRec deployment guide, request section: a positive temperature orders
+// the candidates by a Gumbel-perturbed key, the returned score holds no noise).  With noise
+// (G), the ordering key of a candidate is fl32(key + tg) with tg = fl32(T * g), each an
+// IEEE rounding of its own (no fused multiply-add).  tg of one candidate:
+__device__ __forceinline__ float noise_term(const SelArgs& a, const float* grow, int c, int& fl) {
+  const float g = grow[c];
+  if (!__builtin_isfinite(g)) fl |= GRW_FLAG_BAD_NOISE;
+  return __fmul_rn(a.temp, g);
+}
+
+// The ordering key from the key and tg (the key itself without noise).
+template <bool G>
+__device__ __forceinline__ float order_key(float key, float tg) {
+  if constexpr (G) return __fadd_rn(key, tg);
+  else return key;
+}
+
 // Composite key of one candidate (0 when it is not a candidate), with the precondition flags.
-__device__ __forceinline__ uint64_t candidate(float s, float lp, uint32_t flat, int& fl) {
+template <bool G>
+__device__ __forceinline__ uint64_t candidate(float s, float lp, float tg, uint32_t flat, int& fl) {
   if (__builtin_isnan(lp)) { fl |= GRW_FLAG_NAN_LOGPROB; return 0; }
   if (lp > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
   const float key = s + lp;
   if (key == -INFINITY) return 0;
-  return composite_key(ordered_key(key), flat);
+  const float ok = order_key<G>(key, tg);
+  if (ok == -INFINITY || __builtin_isnan(ok)) return 0;
+  return composite_key(ordered_key(ok), flat);
 }
 
 // Row layouts of the one-read path: kFull — all C codes with C % 4 == 0 and an aligned row,
@@ -337,9 +357,10 @@ __device__ __forceinline__ uint64_t candidate(float s, float lp, uint32_t flat, 
 // thread t holding row positions t + 256 k (their codes are kept).
 enum RowLayout { kFull = 0, kFullScalar = 1, kTrie = 2 };
 
-template <int L>
+template <int L, bool G = false>
 struct RowRegs {
   float lp[kRegC];
+  float tg[G ? kRegC : 1];     // fl32(T * g) of each position (sampled selection)
   int code[L == kTrie ? kRegC : 1];
   __device__ __forceinline__ int code_of(int k) const {
     if constexpr (L == kTrie) return code[k];
@@ -352,31 +373,43 @@ struct RowRegs {
   }
 };
 
-// Read a row of up to kOnePass candidates into registers (one load per candidate).
-// Positions that hold no candidate read as -inf.
-template <int L>
-__device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const float* lprow,
-                                         const int32_t* codes, int cnt, int& fl) {
+// Read a row of up to kOnePass candidates into registers (one load per candidate), and with
+// noise (G) the noise terms of the same positions from grow.  Positions that hold no
+// candidate read as -inf.
+template <int L, bool G = false>
+__device__ __forceinline__ void load_row(RowRegs<L, G>& rr, const SelArgs& a, const float* lprow,
+                                         const float* grow, const int32_t* codes, int cnt, int& fl) {
   const int tid = threadIdx.x;
   if constexpr (L == kFull) {
 #pragma unroll
     for (int q = 0; q < kRegC / 4; ++q) {
       const int i = 4 * (tid + 256 * q);
-      floatx4 x;
+      floatx4 x, y;
       if (i + 3 < cnt) {
         x = *(const floatx4*)(lprow + i);
+        if constexpr (G) y = *(const floatx4*)(grow + i);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = i + e < cnt ? lprow[i + e] : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          x[e] = i + e < cnt ? lprow[i + e] : -INFINITY;
+          if constexpr (G) y[e] = i + e < cnt ? grow[i + e] : 0.0f;
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rr.lp[4 * q + e] = x[e];
+      for (int e = 0; e < 4; ++e) {
+        rr.lp[4 * q + e] = x[e];
+        if constexpr (G) {
+          if (!__builtin_isfinite(y[e])) fl |= GRW_FLAG_BAD_NOISE;
+          rr.tg[4 * q + e] = __fmul_rn(a.temp, y[e]);
+        }
+      }
     }
   } else if constexpr (L == kFullScalar) {
 #pragma unroll
     for (int k = 0; k < kRegC; ++k) {
       const int i = tid + 256 * k;
       rr.lp[k] = i < cnt ? lprow[i] : -INFINITY;
+      if constexpr (G) rr.tg[k] = i < cnt ? noise_term(a, grow, i, fl) : 0.0f;
     }
   } else {
 #pragma unroll
@@ -390,6 +423,7 @@ __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const
       const bool ok = in_row && (unsigned)rr.code[k] < (unsigned)a.C;
       if (in_row && !ok) fl |= GRW_FLAG_BAD_NODE;   // corrupt trie row: never read outside the row
       rr.lp[k] = ok ? lprow[rr.code[k]] : -INFINITY;
+      if constexpr (G) rr.tg[k] = ok ? noise_term(a, grow, rr.code[k], fl) : 0.0f;
       if (!ok) rr.code[k] = -1;
     }
   }
@@ -397,24 +431,26 @@ __device__ __forceinline__ void load_row(RowRegs<L>& rr, const SelArgs& a, const
 
 // Ordered key of candidate k of a loaded row (0 when it is not a candidate or is below
 // tau), with the precondition flags.
-template <int L>
-__device__ __forceinline__ uint32_t row_key(const RowRegs<L>& rr, int k, int cnt, float s, uint32_t tau, int& fl) {
+template <int L, bool G>
+__device__ __forceinline__ uint32_t row_key(const RowRegs<L, G>& rr, int k, int cnt, float s, uint32_t tau, int& fl) {
   if (!rr.valid(k, cnt)) return 0u;
   const float lp = rr.lp[k];
   if (__builtin_isnan(lp)) { fl |= GRW_FLAG_NAN_LOGPROB; return 0u; }
   if (lp > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
   const float key = s + lp;
   if (key == -INFINITY) return 0u;
-  const uint32_t o = ordered_key(key);
+  const float okf = order_key<G>(key, G ? rr.tg[k] : 0.0f);
+  if (okf == -INFINITY || __builtin_isnan(okf)) return 0u;
+  const uint32_t o = ordered_key(okf);
   return o >= tau ? o : 0u;
 }
 
 // The best candidate of a row of up to kOnePass candidates (0 when none).
-template <int L>
-__device__ __forceinline__ uint64_t row_best(const SelArgs& a, const float* lprow, const int32_t* codes, int cnt,
-                                             float s, uint32_t flat_base, int& fl) {
-  RowRegs<L> rr;
-  load_row<L>(rr, a, lprow, codes, cnt, fl);
+template <int L, bool G>
+__device__ __forceinline__ uint64_t row_best(const SelArgs& a, const float* lprow, const float* grow,
+                                             const int32_t* codes, int cnt, float s, uint32_t flat_base, int& fl) {
+  RowRegs<L, G> rr;
+  load_row<L, G>(rr, a, lprow, grow, codes, cnt, fl);
   uint64_t best = 0;
 #pragma unroll
   for (int k = 0; k < kRegC; ++k) {
@@ -427,7 +463,9 @@ __device__ __forceinline__ uint64_t row_best(const SelArgs& a, const float* lpro
 // The row layout of a beam's one-read path.
 __device__ __forceinline__ int row_layout(const SelArgs& a, const int32_t* codes, const float* lprow) {
   if (codes != nullptr) return kTrie;
-  return ((a.C & 3) == 0 && (((uintptr_t)lprow) & 15) == 0) ? kFull : kFullScalar;
+  const bool aligned = (((uintptr_t)lprow) & 15) == 0 &&
+                       (a.noise == nullptr || ((((uintptr_t)a.noise) + (uintptr_t)(lprow - a.logprobs) * 4) & 15) == 0);
+  return ((a.C & 3) == 0 && aligned) ? kFull : kFullScalar;
 }
 
 // Device-coherent access to data that another workgroup, possibly on another XCD, writes
@@ -461,6 +499,7 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 // top_k of its beam) with device-coherent stores and counts itself; the request's last
 // pilot sets bound[r] to the W_r-th best key of all contributions (0 when there are fewer
 // than W_r) and resets the count.
+template <bool G>
 __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   __shared__ uint64_t red64[4];
   __shared__ uint32_t hist[256];
@@ -475,20 +514,22 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   const float s = a.scores[slot];
   const uint32_t flat_base = (uint32_t)(slot - rd.boff) * (uint32_t)a.C;
   const float* lprow = a.logprobs + (size_t)slot * a.C;
+  const float* grow = G ? a.noise + (size_t)slot * a.C : nullptr;
   int cnt = a.C, fl = 0;
   const int32_t* codes = nullptr;
   uint64_t best = 0;
   if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes)) {
     if (cnt <= kOnePass) {
       const int lay = row_layout(a, codes, lprow);
-      if (lay == kFull) best = row_best<kFull>(a, lprow, codes, cnt, s, flat_base, fl);
-      else if (lay == kFullScalar) best = row_best<kFullScalar>(a, lprow, codes, cnt, s, flat_base, fl);
-      else best = row_best<kTrie>(a, lprow, codes, cnt, s, flat_base, fl);
+      if (lay == kFull) best = row_best<kFull, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
+      else if (lay == kFullScalar) best = row_best<kFullScalar, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
+      else best = row_best<kTrie, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
     } else {
       for (int q = tid; q < cnt; q += 256) {
         const int c = codes ? codes[q] : q;
         if ((unsigned)c >= (unsigned)a.C) continue;
-        best = max(best, candidate(s, lprow[c], flat_base + (uint32_t)c, fl));
+        const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
+        best = max(best, candidate<G>(s, lprow[c], tg, flat_base + (uint32_t)c, fl));
       }
     }
   }
@@ -505,12 +546,13 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   if (tid % gsz == 0) st_dev(&a.pilot_buf[pd.z + tid / gsz], best);
   wait_stores();
   __syncthreads();
-  if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(rd.n_pilot - 1);
+  const int n_pilot = G ? rd.n_pilot_s : rd.n_pilot;
+  if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(n_pilot - 1);
   __syncthreads();
   if (!last_s) return;
   // the W_r-th best key of all contributions bounds the request's W_r-th best pool entry
   constexpr int NP = kPilotCap / 256;
-  const int n_ent = rd.n_pilot * (256 / gsz);
+  const int n_ent = n_pilot * (256 / gsz);
   const uint64_t* pb = a.pilot_buf + rd.pilot_off;
   uint32_t pk[NP];
   int nv = 0;
@@ -535,6 +577,7 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
 // --------------------------------------------------------------------------------------
 // Rows of any length (used when C > kOnePass): rows of up to kOnePass candidates in
 // registers as above; longer rows stream through the LDS buffer.
+template <bool G>
 __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
   __shared__ uint64_t buf[kSelCap];
   __shared__ uint32_t hist[256];
@@ -552,14 +595,16 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
   int cnt = 0;
   const int32_t* codes = nullptr;
   uint32_t tau = a.bound[r];
-  // a beam below the bound keeps nothing: no key exceeds its beam's score
-  bool live = s != -INFINITY && !__builtin_isnan(s) && ordered_key(s) >= tau;
+  // a beam below the bound keeps nothing: no key exceeds its beam's score (noise can lift
+  // an ordering key above the score, so the sampled selection reads every live beam)
+  bool live = s != -INFINITY && !__builtin_isnan(s) && (G || ordered_key(s) >= tau);
   if (__builtin_isnan(s)) fl |= GRW_FLAG_NAN_LOGPROB;
   if (live && !beam_row(a, slot, cnt, codes)) {
     fl |= GRW_FLAG_BAD_NODE;
     live = false;
   }
   const float* lprow = a.logprobs + (size_t)slot * a.C;
+  const float* grow = G ? a.noise + (size_t)slot * a.C : nullptr;
   const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * rd.K;
   const int K = rd.K;
@@ -569,15 +614,16 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
     // ---- one pass: the row in registers, filtered by the bound, top K kept ----
     uint64_t v[kRegC];
     {
-      RowRegs<kTrie> rr;     // row positions t + 256 k, codes kept (also for the full range)
+      RowRegs<kTrie, G> rr;  // row positions t + 256 k, codes kept (also for the full range)
       if (codes != nullptr) {
-        load_row<kTrie>(rr, a, lprow, codes, cnt, fl);
+        load_row<kTrie, G>(rr, a, lprow, grow, codes, cnt, fl);
       } else {
 #pragma unroll
         for (int k = 0; k < kRegC; ++k) {
           const int i = tid + 256 * k;
           rr.code[k] = i < cnt ? i : -1;
           rr.lp[k] = i < cnt ? lprow[i] : 0.0f;
+          if constexpr (G) rr.tg[k] = i < cnt ? noise_term(a, grow, i, fl) : 0.0f;
         }
       }
 #pragma unroll
@@ -638,7 +684,8 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
             fl |= GRW_FLAG_BAD_NODE;
             continue;
           }
-          const uint64_t x = candidate(s, lprow[c], flat_base + (uint32_t)c, fl);
+          const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
+          const uint64_t x = candidate<G>(s, lprow[c], tg, flat_base + (uint32_t)c, fl);
           if (x != 0 && (uint32_t)(x >> 32) >= tau) e[ne++] = x;
         }
       }
@@ -722,15 +769,15 @@ __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int ra
   a.out_node[slot] = node;
 }
 
-// Histogram bin of an entry: ordered-key distance below the origin, scaled down by
-// `shift`, clamped to the NB bins.  Non-increasing in the entry, so the bins order the
-// entries (ties inside a bin are ranked by full comparison).
+// Histogram bin of an entry: its key's distance below the origin in the float domain,
+// times the bin scale, clamped to the NB bins.  Rounded float subtraction and
+// multiplication are monotone, so the bin is non-increasing in the entry and the bins order
+// the entries (ties inside a bin are ranked by full comparison).  The float domain keeps the
+// bins even when the keys straddle zero, where ordered keys jump by about 2^31.
 template <int NB>
-__device__ __forceinline__ int hist_bin(uint64_t v, uint32_t origin, uint32_t shift) {
-  const uint32_t ok = (uint32_t)(v >> 32);
-  const uint32_t d = origin > ok ? origin - ok : 0u;
-  const uint32_t b = d >> shift;
-  return b < (uint32_t)NB ? (int)b : NB - 1;
+__device__ __forceinline__ int hist_bin(uint64_t v, float origin, float scale) {
+  const float d = (origin - float_of_ordered((uint32_t)(v >> 32))) * scale;
+  return d < (float)(NB - 1) ? (d > 0.0f ? (int)d : 0) : NB - 1;
 }
 
 // beam of entry index i: the last b with pre[b] <= i (pre[0] = 0, pre[W] = n > i)
@@ -768,7 +815,7 @@ struct FinalLds {
 // every winner its output position.  When a bin holds more than BINCAP entries, a radix
 // select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
 // device-coherent loads (they may come from other workgroups of the same kernel).
-template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP>
+template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP, bool G = false>
 __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L) {
   constexpr bool EDGES = EDGECAP == WINCAP;   // entries carry their CSR edge (trie rows)
   constexpr int BPT = MAXW / NT;     // beams per thread
@@ -818,16 +865,6 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
   const uint32_t n = L.pre[W];
   const int nsel = min((int)n, W);
 
-  // histogram origin and scale: bins reach from the best live score down to the bound
-  uint32_t lo = ld_dev(&a.bound[r]);
-  if (lo == 0 && smax != 0) {
-    const uint32_t u = (smax & 0x80000000u) ? (smax & 0x7fffffffu) : ~smax;   // inverse ordered key
-    lo = ordered_key(__uint_as_float(u) - 64.0f);
-  }
-  const uint32_t span = smax > lo ? smax - lo : 0u;
-  uint32_t shift = 0;
-  while ((span >> shift) >= (uint32_t)NB - 1) ++shift;
-
   auto entry = [&](uint32_t i) {
     const int b = entry_beam(L.pre, W, i);
     return ld_dev(&pool[(size_t)b * K + (i - L.pre[b])]);
@@ -869,7 +906,30 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
       }
     }
   };
-  for_each_entry([&](uint64_t v, int) { atomicAdd(&L.hcnt[hist_bin<NB>(v, smax, shift)], 1u); });
+  if constexpr (G) {
+    // noise can lift an ordering key above every beam score: the bins start at the best entry
+    uint32_t m = 0;
+    for_each_entry([&](uint64_t v, int) { m = max(m, (uint32_t)(v >> 32)); });
+    m = wave_max(m);
+    __syncthreads();
+    if (lane == 0) L.wmax[wave] = m;
+    __syncthreads();
+    smax = 0;
+    for (int w = 0; w < NT / 64; ++w) smax = max(smax, L.wmax[w]);
+  }
+
+  // histogram origin and scale: bins reach from the best live score (the best entry with
+  // noise) down to the bound
+  uint32_t lo = ld_dev(&a.bound[r]);
+  if (lo == 0 && smax != 0) {
+    const uint32_t u = (smax & 0x80000000u) ? (smax & 0x7fffffffu) : ~smax;   // inverse ordered key
+    lo = ordered_key(__uint_as_float(u) - 64.0f);
+  }
+  const float org = float_of_ordered(smax), lo_f = float_of_ordered(lo);
+  const float width = org - lo_f;      // >= 0; bins of width / (NB - 1)
+  const float scale = width > 0.0f && width < 3.0e38f ? (float)(NB - 1) / width : 0.0f;
+
+  for_each_entry([&](uint64_t v, int) { atomicAdd(&L.hcnt[hist_bin<NB>(v, org, scale)], 1u); });
   __syncthreads();
 
   // bin starts: exclusive scan of the histogram; the bin of the nsel-th entry
@@ -912,7 +972,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
     for (int k = 0; k < HPT; ++k) cursor[tid * HPT + k] = 0u;
     __syncthreads();
     auto place = [&](uint64_t v, int e) {
-      const int b = hist_bin<NB>(v, smax, shift);
+      const int b = hist_bin<NB>(v, org, scale);
       if ((uint32_t)b <= tb) {
         const uint32_t p = L.start[b] + atomicAdd(&cursor[b], 1u);
         if (p < L.start[b + 1]) {
@@ -926,7 +986,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
     const int m = (int)L.start[tb + 1];
     for (int p = tid; p < m; p += NT) {
       const uint64_t v = L.win[p];
-      const int b = hist_bin<NB>(v, smax, shift);
+      const int b = hist_bin<NB>(v, org, scale);
       const int s0 = (int)L.start[b], e0 = (int)L.start[b + 1];
       int rank = s0;
       for (int q = s0; q < e0; ++q) rank += L.win[q] > v;
@@ -984,10 +1044,11 @@ constexpr int kGlobThreads = 1024;
 constexpr int kGlobWinCap = kMaxW + kBinCap;
 typedef FinalLds<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, 1> GlobLds;
 
+template <bool G>
 __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GlobLds& L = *(GlobLds*)smem;
-  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1>(a, blockIdx.x, L);
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G>(a, blockIdx.x, L);
   if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
 }
 
@@ -1040,15 +1101,19 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
 }
 
 // Survivors of one loaded beam row: candidates >= the request's bound, stored in the beam's
-// pool region.  Returns the survivor count, or -1 when the row has more than top_k of them
-// (nothing is stored; the request's W-of-pool workgroup selects that row's top_k).  Reached
-// by every thread of the workgroup.
-template <int L>
-__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L>& rr, int& fl, int* red) {
+// pool region.  Returns the survivor count.  When the row has more than top_k of them:
+// without noise (rare once the bound is set) it returns -1 and stores nothing, and the
+// request's W-of-pool workgroup selects that row's top_k; with noise (G), where it happens
+// to several beams per step, a radix select over the registers keeps the top_k here.
+// Reached by every thread of the workgroup.
+template <int L, bool G>
+__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L, G>& rr, int& fl, int* red,
+                                         uint32_t* hist, uint32_t* scr, uint32_t* red32) {
   const ReqDesc& rd = b.rd;
   const uint32_t tau = b.tau;
-  // a beam below the bound keeps nothing: no key exceeds its beam's score
-  if (!b.live || ordered_key(b.s) < tau) return 0;
+  // a beam below the bound keeps nothing: no key exceeds its beam's score (with noise an
+  // ordering key can exceed it, so every live beam is read)
+  if (!b.live || (!G && ordered_key(b.s) < tau)) return 0;
   const int j = b.slot - rd.boff;
   const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
   // Admission in the float domain: for a non-NaN key, key >= tau_f exactly when its
@@ -1062,7 +1127,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   for (int k = 0; k < kRegC; ++k) {
     const float lp = rr.lp[k];
     suspect |= !(lp <= 0.0f);                    // NaN or positive: a precondition flag
-    na += b.s + lp >= tau_f;
+    na += order_key<G>(b.s + lp, G ? rr.tg[k] : 0.0f) >= tau_f;
   }
   if (suspect) {
 #pragma unroll
@@ -1075,12 +1140,40 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   int p = block_excl_scan<256>(na, red, &n);
   if (n == 0) return 0;
   const int K = rd.K;
-  if (n > K) return -1;
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
   int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
+  if (n > K) {
+    if constexpr (!G) {
+      return -1;
+    } else {
+      auto key = [&](int k) -> uint32_t {
+        const float kf = order_key<G>(b.s + rr.lp[k], rr.tg[k]);
+        return kf >= tau_f ? ordered_key(kf) : 0u;
+      };
+      auto flat = [&](int k) -> uint32_t { return flat_base + (uint32_t)rr.code_of(k); };
+      const uint64_t T = regs_select_composite<256, kRegC>(key, flat, K, n, hist, scr, red32);
+      const uint32_t thi = (uint32_t)(T >> 32), tlo = (uint32_t)T;
+      uint32_t keep = 0;
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k) {
+        const uint32_t ok = key(k);
+        if (ok > thi || (ok == thi && ok != 0u && ~flat(k) >= tlo)) keep |= 1u << k;
+      }
+      int total;
+      int q = block_excl_scan<256>(__builtin_popcount(keep), red, &total);
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k) {
+        if ((keep >> k) & 1u) {
+          if constexpr (L == kTrie) redge[q] = b.beg + (int)threadIdx.x + 256 * k;
+          region[q++] = composite_key(key(k), flat(k));
+        }
+      }
+      return min(total, K);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kRegC; ++k) {
-    const float kf = b.s + rr.lp[k];
+    const float kf = order_key<G>(b.s + rr.lp[k], G ? rr.tg[k] : 0.0f);
     if (kf >= tau_f) {
       if constexpr (L == kTrie) redge[p] = b.beg + (int)threadIdx.x + 256 * k;
       region[p++] = composite_key(ordered_key(kf), flat_base + (uint32_t)rr.code_of(k));
@@ -1093,7 +1186,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
 // by the NT threads of the request's W-of-pool workgroup: the row is read again, NR
 // positions per thread (rows of at most NT * NR candidates), a radix select finds the
 // top_k-th composite, and the survivors go to the beam's pool region.
-template <int NT, int NR>
+template <int NT, int NR, bool G>
 __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd, int r, int slot, uint32_t* hist,
                                              uint32_t* scr, uint32_t* red32, int* red) {
   const int tid = threadIdx.x;
@@ -1110,22 +1203,25 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
   const float* lprow = a.logprobs + (size_t)slot * a.C;
   const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
   const int beg = codes != nullptr ? (int)(codes - a.code) : 0;
+  const float* grow = G ? a.noise + (size_t)slot * a.C : nullptr;
   float lp[NR];
+  float tg[G ? NR : 1];
   int code[NR];
-  int na = 0;
+  int na = 0, fl = 0;
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     const int i = tid + NT * k;
     code[k] = i < cnt ? (codes != nullptr ? codes[i] : i) : -1;
     if ((unsigned)code[k] >= (unsigned)a.C) code[k] = -1;
     lp[k] = code[k] >= 0 ? lprow[code[k]] : -INFINITY;
-    na += s + lp[k] >= tau_f;
+    if constexpr (G) tg[k] = code[k] >= 0 ? noise_term(a, grow, code[k], fl) : 0.0f;
+    na += order_key<G>(s + lp[k], G ? tg[k] : 0.0f) >= tau_f;
   }
   int n;
   (void)block_excl_scan<NT>(na, red, &n);
   const int K = rd.K;
   auto key = [&](int k) -> uint32_t {
-    const float kf = s + lp[k];
+    const float kf = order_key<G>(s + lp[k], G ? tg[k] : 0.0f);
     return kf >= tau_f ? ordered_key(kf) : 0u;
   };
   auto flat = [&](int k) -> uint32_t { return flat_base + (uint32_t)code[k]; };
@@ -1152,18 +1248,21 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
 }
 
 // Per-beam stage: survivors of each beam slot (candidates >= the request's bound) into the
-// slot's pool region, and the slot's survivor count (-1: more than top_k, left to the
-// W-of-pool stage).
-template <int L>
+// slot's pool region, and the slot's survivor count (-1: more than top_k without noise,
+// left to the W-of-pool stage).
+template <int L, bool G>
 __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   __shared__ int red[4];
+  __shared__ uint32_t hist[G ? 256 : 1];
+  __shared__ uint32_t scr[4];
+  __shared__ uint32_t red32[8];
   const int tid = threadIdx.x;
   const int slot = blockIdx.x;
   int fl = 0;
   const BeamRow b = beam_setup(a, slot, fl);
-  RowRegs<L> rr;
-  if (b.live) load_row<L>(rr, a, b.lprow, b.codes, b.cnt, fl);
-  const int n_out = keep_beam<L>(a, b, rr, fl, red);
+  RowRegs<L, G> rr;
+  if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl);
+  const int n_out = keep_beam<L, G>(a, b, rr, fl, red, hist, scr, red32);
   if (tid == 0) a.surv_count[slot] = n_out;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
@@ -1175,6 +1274,7 @@ __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
 constexpr int kFinThreads = 1024;
 typedef FinalLds<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedWinCap> FinLds;
 
+template <bool G>
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   FinLds& L = *(FinLds*)smem;
@@ -1193,11 +1293,11 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   for (int i = 0; i < no; ++i) {
     const int slot = (int)L.pre[i];
     __syncthreads();
-    overflow_row<kFinThreads, kOnePass / kFinThreads>(a, rd, r, slot, L.hist, L.scr, red32, red);
+    overflow_row<kFinThreads, kOnePass / kFinThreads, G>(a, rd, r, slot, L.hist, L.scr, red32, red);
   }
   wait_stores();
   __syncthreads();
-  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap>(a, r, L);
+  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G>(a, r, L);
   __syncthreads();
   if (threadIdx.x == 0) a.bound[r] = 0u;
 }
@@ -1239,47 +1339,63 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 }  // namespace
 
+template <bool G>
+hipError_t select_topk_path(const SelArgs& a, hipStream_t s) {
+  select_pilot_kernel<G><<<a.n_pilots, 256, 0, s>>>(a);
+  select_topk_kernel<G><<<a.sumW, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_topk(const SelArgs& a, hipStream_t s) {
   if (a.sumW == 0) return hipSuccess;
-  select_pilot_kernel<<<a.n_pilots, 256, 0, s>>>(a);
-  select_topk_kernel<<<a.sumW, 256, 0, s>>>(a);
+  return a.noise != nullptr ? select_topk_path<true>(a, s) : select_topk_path<false>(a, s);
+}
+
+template <bool G>
+hipError_t select_global_path(const SelArgs& a, hipStream_t s) {
+  static bool attr_set = false;   // the bin arrays and winner array exceed the default 64 KB
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)select_global_kernel<G>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GlobLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  select_global_kernel<G><<<a.R, kGlobThreads, sizeof(GlobLds), s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_global(const SelArgs& a, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  static bool attr_set = false;   // the bin arrays and winner array exceed the default 64 KB
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_global_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GlobLds));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  select_global_kernel<<<a.R, kGlobThreads, sizeof(GlobLds), s>>>(a);
-  return hipGetLastError();
+  return a.noise != nullptr ? select_global_path<true>(a, s) : select_global_path<false>(a, s);
 }
 
 bool select_fused_ok(int C, int max_W) { return C <= kOnePass && max_W <= kFusedMaxW; }
 
-hipError_t launch_select_fused(const SelArgs& a, hipStream_t s) {
-  if (a.sumW == 0) return hipSuccess;
+template <bool G>
+hipError_t select_fused_path(const SelArgs& a, hipStream_t s) {
   static bool attr_set = false;   // the W-of-pool select's arrays exceed the default 64 KB
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_final_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)select_final_kernel<G>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinLds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  select_pilot_kernel<<<a.n_pilots, 256, 0, s>>>(a);
+  select_pilot_kernel<G><<<a.n_pilots, 256, 0, s>>>(a);
   const int grid = a.sumW;
+  const bool aligned = (((uintptr_t)a.logprobs) & 15) == 0 && (!G || (((uintptr_t)a.noise) & 15) == 0);
   if (a.row_ptr != nullptr)
-    select_beam_kernel<kTrie><<<grid, 256, 0, s>>>(a);
-  else if ((a.C & 3) == 0 && (((uintptr_t)a.logprobs) & 15) == 0)
-    select_beam_kernel<kFull><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kTrie, G><<<grid, 256, 0, s>>>(a);
+  else if ((a.C & 3) == 0 && aligned)
+    select_beam_kernel<kFull, G><<<grid, 256, 0, s>>>(a);
   else
-    select_beam_kernel<kFullScalar><<<grid, 256, 0, s>>>(a);
-  select_final_kernel<<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
+    select_beam_kernel<kFullScalar, G><<<grid, 256, 0, s>>>(a);
+  select_final_kernel<G><<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_select_fused(const SelArgs& a, hipStream_t s) {
+  if (a.sumW == 0) return hipSuccess;
+  return a.noise != nullptr ? select_fused_path<true>(a, s) : select_fused_path<false>(a, s);
 }
 
 hipError_t launch_beams_init(const ReqDesc* req, const int32_t* slot_req, int32_t sumW,

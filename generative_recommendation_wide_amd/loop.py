@@ -29,28 +29,36 @@ class DecodeLoop:
         self.parents = torch.empty(S, sumW, dtype=torch.int32, device=dev)   # parent_idx
         self.sid = torch.empty(sumW, S, dtype=torch.int32, device=dev)
 
-    def select_step(self, d: int, logprobs, stream=None):
-        from . import beam_select
+    def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0):
+        """Selection at depth d; with noise, the Gumbel top-k at the given temperature."""
+        from . import beam_select, beam_select_gumbel
         cur, nxt = d % 2, (d + 1) % 2
         row_ptr, code, n_int = self.trie if self.trie is not None else (None, None, 0)
-        beam_select(self.ws, logprobs, self.scores[cur], self.nodes[cur], row_ptr, code, n_int,
-                    self.W, self.K, self.C, self.tokens[d], self.parents[d], self.scores[nxt],
-                    self.nodes[nxt], stream)
+        if noise is None:
+            beam_select(self.ws, logprobs, self.scores[cur], self.nodes[cur], row_ptr, code, n_int,
+                        self.W, self.K, self.C, self.tokens[d], self.parents[d], self.scores[nxt],
+                        self.nodes[nxt], stream)
+        else:
+            beam_select_gumbel(self.ws, logprobs, noise, temperature, self.scores[cur], self.nodes[cur],
+                               row_ptr, code, n_int, self.W, self.K, self.C, self.tokens[d], self.parents[d],
+                               self.scores[nxt], self.nodes[nxt], stream)
 
     def attn_step(self, d: int, layer, out, stream=None):
         from . import beam_attn_decode
         beam_attn_decode(self.ws, layer["q"][d], layer["k_s"], layer["v_s"], layer.get("k_scale"),
                          layer.get("v_scale"), layer["k_u"], layer["v_u"], self.parents, d, out, stream)
 
-    def run(self, logprobs, layers, out, stream=None, steps=None):
+    def run(self, logprobs, layers, out, stream=None, steps=None, noise=None, temperature: float = 0.0):
         """logprobs: sequence of S device tensors [sumW][C]; layers: sequence of dicts with
         q [S][sumW][Hq][D], k_s, v_s, k_scale, v_scale, k_u, v_u (device tensors);
-        out: [sumW][Hq][D] float32 device tensor, or a list with one per layer."""
+        out: [sumW][Hq][D] float32 device tensor, or a list with one per layer;
+        noise: None, or a sequence of S device tensors [sumW][C] of Gumbel draws for the
+        sampled selection at the given temperature."""
         from . import grw_backtrack
         steps = self.S if steps is None else steps
         self.ws.beams_init(self.scores[0], self.nodes[0], stream)
         for d in range(steps):
-            self.select_step(d, logprobs[d], stream)
+            self.select_step(d, logprobs[d], stream, None if noise is None else noise[d], temperature)
             for li, layer in enumerate(layers):
                 self.attn_step(d, layer, out[li] if isinstance(out, (list, tuple)) else out, stream)
         if steps == self.S:

@@ -3,6 +3,7 @@
  *
  * One decode step of wide-beam generative recommendation:
  *   beam_select       trie-masked per-beam top_k, then the global beam_width-of-pool select
+ *   beam_select_gumbel the same with Gumbel-perturbed ordering keys (temperature > 0)
  *   beam_attn_decode  beam attention over a shared prompt KV plus per-beam decode KV
  *                     reached through parent pointers, in three stages
  *                     (shared stage, unshared stage, online-softmax merge)
@@ -69,7 +70,8 @@ enum grw_device_flag {
   GRW_FLAG_BAD_NODE = 4,        /* a live beam's trie node is outside [0, n_internal)       */
   GRW_FLAG_BAD_PARENT = 8,      /* a parent pointer walk left [0, W_r)                       */
   GRW_FLAG_CHILD_MISSING = 16,  /* a selected code is not a child of its parent's node      */
-  GRW_FLAG_POOL_CORRUPT = 32    /* internal check: a pool entry names a slot outside W_r    */
+  GRW_FLAG_POOL_CORRUPT = 32,   /* internal check: a pool entry names a slot outside W_r    */
+  GRW_FLAG_BAD_NOISE = 64       /* a Gumbel noise value of the sampled selection is not finite */
 };
 
 /*
@@ -207,6 +209,34 @@ int beam_select(grw_ws* ws, const float* logprobs, const float* beam_scores,
                 const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K,
                 int32_t C, int32_t* out_token, int32_t* out_parent, float* out_score,
                 int32_t* out_node, void* stream);
+
+/*
+ * beam_select_gumbel — the sampled selection step: Gumbel top-k at a positive temperature
+ * (FlashRec deployment guide, request section: temperature 0 is the deterministic top-k,
+ * a positive temperature a Gumbel top-k whose noise only orders the candidates; the
+ * returned sequence score holds no noise).
+ *
+ * Same candidates, tie rules, outputs and early exit as beam_select, except that every
+ * top_k and beam_width decision orders candidate (b, c) by
+ *   okey(b, c) = fl32(key(b, c) + fl32(temperature * noise[b][c]))
+ * (two IEEE roundings, no fused multiply-add) in place of key(b, c); a candidate whose okey
+ * is -inf is dropped.  out_score is still key(b, c), so the next step's beam scores carry
+ * no noise.  With temperature 0 the result equals beam_select's.  The library draws no
+ * random numbers: noise is the caller's, typically standard Gumbel draws -log(-log(u)).
+ * Noise can lift an ordering key above its beam's score, so the score-based skip of whole
+ * beams is off; the bound on the W_r-th best ordering key still prunes candidates.
+ *
+ *   noise        [sumW][C] float32, row-major like logprobs; must be finite
+ *                (GRW_FLAG_BAD_NOISE reports a non-finite value)
+ *   temperature  finite, >= 0 (else GRW_EINVAL, nothing enqueued)
+ *   other arguments as for beam_select
+ */
+int beam_select_gumbel(grw_ws* ws, const float* logprobs, const float* noise, float temperature,
+                       const float* beam_scores, const int32_t* beam_node,
+                       const int32_t* trie_row_ptr, const int32_t* trie_code,
+                       int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
+                       int32_t* out_token, int32_t* out_parent, float* out_score,
+                       int32_t* out_node, void* stream);
 
 /*
  * grw_backtrack — the semantic-ID tuple of every final beam (xLLM design doc, section

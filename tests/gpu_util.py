@@ -33,9 +33,11 @@ def trie_device(trie):
             int(trie["n_internal"]))
 
 
-def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label=""):
+def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
+                          noise_of_step=None, temperature=0.0):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
-    every checked request bit-exactly with oracle_select at every step.  Returns the loop."""
+    every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
+    the steps are the Gumbel-sampled selection at the given temperature.  Returns the loop."""
     Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
     R = len(Ws)
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
@@ -49,7 +51,10 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
     pools = {}
     for d in range(S):
         lp = lp_of_step(d)
-        loop.select_step(d, torch.from_numpy(np.ascontiguousarray(lp)).cuda())
+        g = noise_of_step(d) if noise_of_step is not None else None
+        loop.select_step(d, torch.from_numpy(np.ascontiguousarray(lp)).cuda(),
+                         noise=None if g is None else torch.from_numpy(np.ascontiguousarray(g)).cuda(),
+                         temperature=temperature)
         torch.cuda.synchronize()
         tok = loop.tokens[d].cpu().numpy()
         par = loop.parents[d].cpu().numpy()
@@ -58,7 +63,8 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
         for r in check:
             a, W = boff[r], Ws[r]
             scores, prefixes = state[r]
-            res = oracle_select(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets)
+            res = oracle_select(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets,
+                                None if g is None else g[a:a + W], temperature)
             where = f"{label} step {d} request {r}"
             np.testing.assert_array_equal(tok[a:a + W], res["tokens"], err_msg=where + " tokens")
             np.testing.assert_array_equal(par[a:a + W], res["parents"], err_msg=where + " parents")
