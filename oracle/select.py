@@ -21,6 +21,10 @@ Readings where the pages are silent (each is the plainest one the rest supports)
 * at level 0 only slot 0 is live (score 0, empty prefix);
 * code c is valid for a beam with prefix p at level l iff p + (c,) is the length-(l+1)
   prefix of some catalog item (decided from the raw item list);
+* selection from raw logits (the fused variant): lse_b = float32(ln sum_c exp(x_bc)) over
+  the whole row of C codes, evaluated in float64 and rounded once, and lp = float32(x - lse_b)
+  by one float32 subtraction; rounding the row's lse before the subtraction confines any
+  difference between two float64 evaluations to that one rounding per row;
 * Gumbel top-k at temperature T >= 0 with noise g (standard Gumbel draws, an input): the
   ordering key of (b, c) is float32(key + float32(T * g[b, c])), two IEEE roundings;
   every top_k / beam_width decision and tie rule above uses it in place of the key, and
@@ -118,6 +122,37 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=
     pool_size = int(sum(k.size for k in pool_key))
     return dict(tokens=tokens, parents=parents, scores=out_scores, prefixes=new_prefixes,
                 pool_size=pool_size)
+
+
+def oracle_log_softmax_rows(logits):
+    """Log-softmax of raw logit rows as the fused selection defines it.
+
+    lse_b = float32(ln sum_c exp(x_bc)), evaluated in float64 as m + ln(sum exp(x - m)) with
+    m the row max and rounded once to float32; lp_bc = float32(x_bc - lse_b), one float32
+    subtraction.  Logits are finite or -inf, at least one finite per row.
+    Returns (lp float32 [n][C], lse float32 [n]).
+    """
+    x32 = np.asarray(logits, dtype=np.float32)
+    assert not np.isnan(x32).any() and not np.isposinf(x32).any()
+    x = x32.astype(np.float64)
+    m = x.max(axis=1)
+    assert np.isfinite(m).all(), "a row without a finite logit"
+    lse = (m + np.log(np.exp(x - m[:, None]).sum(axis=1))).astype(np.float32)
+    lp = x32 - lse[:, None]                      # float32 - float32
+    assert lp.dtype == np.float32
+    return lp, lse
+
+
+def oracle_select_logits(logits, scores, prefixes, level, K, W, C, prefix_sets=None, noise=None,
+                         temperature=0.0):
+    """The selection step from raw logits: log-softmax of every live row over all C codes
+    (oracle_log_softmax_rows), then oracle_select on the result."""
+    scores = np.asarray(scores, dtype=np.float32)
+    lp = np.zeros(np.shape(logits), np.float32)
+    live = scores != NEG_INF
+    if live.any():
+        lp[live] = oracle_log_softmax_rows(np.asarray(logits, np.float32)[live])[0]
+    return oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets, noise, temperature)
 
 
 def initial_beams(W):

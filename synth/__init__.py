@@ -3,7 +3,7 @@
 This package is shared by the oracle side (tests, cpu baseline) and the GPU side
 (tests, bench).  It produces inputs only: catalogs of semantic-ID items, the CSR
 layout of their prefix trie, attention tensors in their storage formats, and
-log-probability rows and the noise rows of the sampled selection.  It holds none of the attention or selection arithmetic.
+log-probability rows, raw logit rows, and the noise rows of the sampled selection.  It holds none of the attention or selection arithmetic.
 """
 from .workloads import (  # noqa: F401
     Workload,
@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     attention_layer,
     logprob_rows,
     gumbel_rows,
+    logit_rows,
     random_parents,
     pack_prefix,
     bf16_bits_from_f32,

@@ -386,3 +386,18 @@ def gumbel_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None):
     if rows is not None:
         out = out[np.asarray(rows)]
     return out
+
+
+def logit_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None):
+    """Raw logits [sumW][C] float32 of one decode step: the N(0, sigma) draws from which
+    logprob_rows takes its log-softmax, rounded once to float32 (the input of the selection
+    from raw logits)."""
+    if wl.name == "ultra5000":
+        raise NotImplementedError("raw logit rows are not generated for the ultra-wide workload")
+    W, K, P = shapes if shapes is not None else request_shapes(wl, seed)
+    sumW = int(W.sum())
+    g = _rng(seed, wl, _S_LOGITS, step)
+    x = (g.standard_normal((sumW, wl.C)) * wl.logit_sigma).astype(np.float32)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    return x

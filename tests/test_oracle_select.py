@@ -15,6 +15,12 @@ float32(key + float32(T * g)); G2 T = 0 reduces exactly to the deterministic sel
 the Gumbel-max law: with one live beam and W = K = 1 the selected code is distributed as
 softmax(lp / T) (chi-square over 20 000 draws); G4 the returned scores hold no noise and the
 outputs are ordered by the perturbed key.
+
+Selection from raw logits: L1 the row lse equals scipy's logsumexp rounded to float32, and
+exp(lp) sums to 1; L2 with logits that already are log-probabilities rounded from a float64
+log-softmax, the lse is ~0 and the selection matches the log-probability oracle up to the
+rounding of that lse; L3 adding a power of two to a row's logits, when it keeps every logit's
+bits exact, leaves that row's lp unchanged.
 """
 import os
 import struct
@@ -381,3 +387,66 @@ def test_gumbel_scores_exclude_noise_and_order_by_perturbed_key():
         assert all((okey[i] > okey[i + 1]) or (okey[i] == okey[i + 1] and flat[i] < flat[i + 1])
                    for i in range(n - 1))
         scores, prefixes = res["scores"], res["prefixes"]
+
+
+def _logit_rows(seed, n, C, sigma=3.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((n, C)) * sigma).astype(np.float32)
+
+
+def test_logits_lse_matches_library_logsumexp():
+    """L1."""
+    from scipy.special import logsumexp
+    from oracle.select import oracle_log_softmax_rows
+    for seed, (n, C) in enumerate([(64, 8192), (300, 257), (5, 3)]):
+        x = _logit_rows(seed, n, C)
+        x[0, : C // 2] = -np.inf                # masked logits
+        lp, lse = oracle_log_softmax_rows(x)
+        ref = logsumexp(x.astype(np.float64), axis=1)
+        assert lse.tolist() == ref.astype(np.float32).tolist()
+        s = np.exp(lp.astype(np.float64)).sum(axis=1)
+        assert np.all(np.abs(s - 1.0) < 1e-5)
+        assert (lp <= 0).all()
+
+
+def test_logits_selection_equals_logprob_selection_for_normalised_rows():
+    """L2: rows that are already log-softmax outputs have lse within float32 rounding of 0."""
+    from oracle.select import oracle_select_logits
+    wl = workload("qwen06b")
+    from synth import request_shapes
+    W, K, P = request_shapes(wl)
+    w, k = int(W[0]), int(K[0])
+    items = catalog_items(wl)
+    psets = catalog_prefix_sets(items, wl.C)
+    scores, prefixes = initial_beams(w)
+    for d in range(wl.S):
+        lp = logprob_rows(wl, d)[:w]
+        a = oracle_select(lp, scores, prefixes, d, k, w, wl.C, psets)
+        b = oracle_select_logits(lp, scores, prefixes, d, k, w, wl.C, psets)
+        # the lse of a normalised row is 0 up to float64 rounding; where it rounds to 0 in
+        # float32 the two selections are identical
+        from oracle.select import oracle_log_softmax_rows
+        live = scores != -np.inf
+        lse = oracle_log_softmax_rows(lp[live])[1]
+        assert np.all(np.abs(lse) < 1e-6)
+        if np.all(lse == 0):
+            assert a["tokens"].tolist() == b["tokens"].tolist()
+            assert a["parents"].tolist() == b["parents"].tolist()
+            assert a["scores"].view(np.uint32).tolist() == b["scores"].view(np.uint32).tolist()
+        scores, prefixes = a["scores"], a["prefixes"]
+
+
+def test_logits_shift_by_exact_power_of_two():
+    """L3: rows whose lse lies in [16, 32) before and after adding 2 to every logit (exact in
+    float32 for logits on a 1/64 grid): the float32 lse moves by exactly 2 and lp keeps its
+    bits, as ln-sum-exp is shift-equivariant and both roundings see the same grid."""
+    from oracle.select import oracle_log_softmax_rows
+    rng = np.random.default_rng(9)
+    x = (np.round(rng.standard_normal((64, 512)) * 64) / 64 + 16.0).astype(np.float32)
+    y = (x + np.float32(2.0)).astype(np.float32)
+    assert np.array_equal(y - np.float32(2.0), x)          # the shift is exact
+    lp0, lse0 = oracle_log_softmax_rows(x)
+    lp1, lse1 = oracle_log_softmax_rows(y)
+    assert np.all((lse0 >= 16) & (lse1 < 32))
+    assert np.array_equal(lse1, lse0 + np.float32(2.0))
+    assert np.array_equal(lp0.view(np.uint32), lp1.view(np.uint32))
