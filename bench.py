@@ -185,13 +185,15 @@ def stage_timings(wl, st, reps):
     return res
 
 
-def select_roofline(seed, dev, reps, temperature=None):
+def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
     """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
     262144-entry pools): device time of one call with every beam live (the third decode step,
     beams from two real selections), against the HBM time of its algorithmic bytes: every
     beam's log-probability row, the beam scores, and the four output arrays.  With a
     temperature, beam_select_gumbel with standard Gumbel noise rows (one more row per beam
-    in the algorithmic bytes)."""
+    in the algorithmic bytes).  With raw_logits, beam_select_logits on the raw logit rows (the
+    log-softmax fused in; the same algorithmic bytes), and beside it the time of torch's
+    float32 log_softmax followed by beam_select."""
     import torch
 
     import generative_recommendation_wide_amd as grw
@@ -203,7 +205,10 @@ def select_roofline(seed, dev, reps, temperature=None):
     lps = []
     for _ in range(3):
         x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
-        lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
+        if raw_logits:
+            lps.append(x.to(torch.float32))
+        else:
+            lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
         del x
     noise = [None] * 3
     if temperature is not None:
@@ -217,8 +222,8 @@ def select_roofline(seed, dev, reps, temperature=None):
     ws.bind_batch(W, K, P)
     loop = grw.DecodeLoop(ws, wl.S, C, None, device=dev)
     ws.beams_init(loop.scores[0], loop.nodes[0])
-    loop.select_step(0, lps[0], noise=noise[0], temperature=temperature or 0.0)
-    loop.select_step(1, lps[1], noise=noise[1], temperature=temperature or 0.0)
+    loop.select_step(0, lps[0], noise=noise[0], temperature=temperature or 0.0, raw_logits=raw_logits)
+    loop.select_step(1, lps[1], noise=noise[1], temperature=temperature or 0.0, raw_logits=raw_logits)
     sc, nd = loop.scores[0].clone(), loop.nodes[0].clone()     # step-2 input beams
     live = int((sc > float("-inf")).sum())
     tok, par = torch.empty(sumW, dtype=torch.int32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
@@ -227,7 +232,10 @@ def select_roofline(seed, dev, reps, temperature=None):
     Wm, Km = int(W.max()), int(K.max())
 
     def fn():
-        if temperature is None:
+        if raw_logits:
+            grw.beam_select_logits(ws, lps[2], noise[2], temperature or 0.0, sc, nd, None, None, 0, Wm, Km, C, tok,
+                                   par, osc, ond)
+        elif temperature is None:
             grw.beam_select(ws, lps[2], sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
         else:
             grw.beam_select_gumbel(ws, lps[2], noise[2], temperature, sc, nd, None, None, 0, Wm, Km, C, tok, par,
@@ -254,6 +262,14 @@ def select_roofline(seed, dev, reps, temperature=None):
     del graph
     same = bool(torch.equal(tok, ref[0]) and torch.equal(par, ref[1]) and
                 torch.equal(osc.view(torch.int32), ref[2].view(torch.int32)))
+    unfused = None
+    if raw_logits and temperature is None:
+        lp_buf = torch.empty_like(lps[2])
+
+        def fn2():
+            torch.log_softmax(lps[2], dim=-1, out=lp_buf)
+            grw.beam_select(ws, lp_buf, sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+        unfused = time_stage(fn2, reps, stream) * 1e3
     pools = [ws.pool_size(r) for r in range(len(W))]
     bytes_ = sumW * C * 4.0 * (1 if temperature is None else 2) + sumW * 4.0 + sumW * 16.0
     t = ms / 1e3
@@ -265,7 +281,9 @@ def select_roofline(seed, dev, reps, temperature=None):
             "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
             "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
             "kernels": "select_pilot_kernel + select_beam_kernel + select_final_kernel",
-            "entry_point": "beam_select" if temperature is None else f"beam_select_gumbel (temperature {temperature})"}
+            "entry_point": ("beam_select_logits" if raw_logits else "beam_select_gumbel" if temperature is not None
+                            else "beam_select") + ("" if temperature is None else f" (temperature {temperature})"),
+            "unfused_log_softmax_then_select_us": None if unfused is None else round(unfused, 2)}
 
 
 # ----------------------------------------------------------------------------------------
@@ -443,6 +461,8 @@ def main():
                     help="only the beam_select measurement on the unconstrained wide pool (for kernel traces)")
     ap.add_argument("--select-temperature", type=float, default=None,
                     help="with --select-only: time beam_select_gumbel at this temperature")
+    ap.add_argument("--select-logits", action="store_true",
+                    help="with --select-only: time beam_select_logits on raw logits")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -468,7 +488,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.select_only:
-        print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature)), flush=True)
+        print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature,
+                                         raw_logits=args.select_logits)), flush=True)
         return 0
     log(f"[bench] setting up {wl.name} ...")
     t_setup = time.perf_counter()
@@ -520,12 +541,14 @@ def main():
                 "kernel": DOMINANT, "flops_per_launch": flops, "avg_launch_us": round(t_shared * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_,
                 "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1)}
-    sel_roof = sel_gumbel = None
+    sel_roof = sel_gumbel = sel_logits = None
     if args.stage_reps > 0:
         sel_roof = select_roofline(args.seed, dev, 20 * args.stage_reps)
         log(f"[bench] select on wide512u: {sel_roof}")
         sel_gumbel = select_roofline(args.seed, dev, 20 * args.stage_reps, temperature=1.0)
         log(f"[bench] Gumbel select on wide512u: {sel_gumbel}")
+        sel_logits = select_roofline(args.seed, dev, 20 * args.stage_reps, raw_logits=True)
+        log(f"[bench] select from raw logits on wide512u: {sel_logits}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -563,6 +586,7 @@ def main():
         "roofline": roofline,
         "select_roofline": sel_roof,
         "select_gumbel_roofline": sel_gumbel,
+        "select_logits_roofline": sel_logits,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

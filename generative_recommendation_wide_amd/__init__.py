@@ -146,6 +146,19 @@ def beam_select_gumbel(ws: Workspace, logprobs, noise, temperature: float, beam_
         _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
 
 
+def beam_select_logits(ws: Workspace, logits, noise, temperature: float, beam_scores, beam_node,
+                       trie_row_ptr, trie_code, trie_n_internal: int, W: int, K: int, C: int,
+                       out_token, out_parent, out_score, out_node, stream=None):
+    """The selection step from raw logits, log-softmax fused in; noise None for the
+    deterministic selection (see include/grw.h)."""
+    _lib.check("beam_select_logits", _L.beam_select_logits(
+        ws.handle, _ptr(logits, _F32, "logits"), _ptr(noise, _F32, "noise"), float(temperature),
+        _ptr(beam_scores, _F32, "beam_scores"), _ptr(beam_node, _I32, "beam_node"),
+        _ptr(trie_row_ptr, _I32, "trie_row_ptr"), _ptr(trie_code, _I32, "trie_code"), int(trie_n_internal),
+        int(W), int(K), int(C), _ptr(out_token, _I32, "out_token"), _ptr(out_parent, _I32, "out_parent"),
+        _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
+
+
 def grw_backtrack(ws: Workspace, tokens, parents, S: int, sid_out, stream=None):
     """Semantic-ID tuples [sumW][S] of the final beams (see include/grw.h)."""
     _lib.check("grw_backtrack", _L.grw_backtrack(

@@ -36,6 +36,7 @@ struct grw_ws {
   int32_t* d_surv_count = nullptr;
   uint32_t* d_bound = nullptr;
   int32_t* d_pilot_desc = nullptr;
+  float* d_row_lse = nullptr;       // [max_total_beams] row lse of the selection from raw logits
   uint64_t* d_pilot_buf = nullptr;
   uint32_t* d_step_state = nullptr;    // [max_requests]: pilots finished in the current step
   int32_t* d_flags = nullptr;
@@ -90,6 +91,7 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_surv_count);
   (void)hipFree(w->d_bound);
   (void)hipFree(w->d_pilot_desc);
+  (void)hipFree(w->d_row_lse);
   (void)hipFree(w->d_step_state);
   (void)hipFree(w->d_pilot_buf);
   (void)hipFree(w->d_flags);
@@ -267,6 +269,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_surv_count, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 8 * B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_row_lse, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_step_state, (int64_t)L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
@@ -468,7 +471,7 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
 namespace {
 
 // One selection step, deterministic (noise == NULL) or Gumbel-sampled.
-int select_step(grw_ws* w, const float* logprobs, const float* noise, float temperature,
+int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* noise, float temperature,
                 const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
                 const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
                 int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream) {
@@ -490,6 +493,8 @@ int select_step(grw_ws* w, const float* logprobs, const float* noise, float temp
   a.logprobs = logprobs;
   a.noise = noise;
   a.temp = noise != nullptr ? temperature : 0.0f;
+  a.row_lse = raw_logits ? w->d_row_lse : nullptr;
+  a.lse_ready = select_fused_ok(C, w->maxW) ? 0 : 1;
   a.scores = beam_scores;
   a.nodes = beam_node;
   a.row_ptr = trie ? trie_row_ptr : nullptr;
@@ -528,7 +533,17 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
                 const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
                 int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
                 float* out_score, int32_t* out_node, void* stream) {
-  return select_step(w, logprobs, nullptr, 0.0f, beam_scores, beam_node, trie_row_ptr, trie_code,
+  return select_step(w, logprobs, false, nullptr, 0.0f, beam_scores, beam_node, trie_row_ptr, trie_code,
+                     trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
+}
+
+int beam_select_logits(grw_ws* w, const float* logits, const float* noise, float temperature,
+                       const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
+                       const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K,
+                       int32_t C, int32_t* out_token, int32_t* out_parent, float* out_score,
+                       int32_t* out_node, void* stream) {
+  if (noise && (!(temperature >= 0.0f) || !std::isfinite(temperature))) return GRW_EINVAL;
+  return select_step(w, logits, true, noise, temperature, beam_scores, beam_node, trie_row_ptr, trie_code,
                      trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
 }
 
@@ -538,7 +553,7 @@ int beam_select_gumbel(grw_ws* w, const float* logprobs, const float* noise, flo
                        int32_t C, int32_t* out_token, int32_t* out_parent, float* out_score,
                        int32_t* out_node, void* stream) {
   if (!noise || !(temperature >= 0.0f) || !std::isfinite(temperature)) return GRW_EINVAL;
-  return select_step(w, logprobs, noise, temperature, beam_scores, beam_node, trie_row_ptr, trie_code,
+  return select_step(w, logprobs, false, noise, temperature, beam_scores, beam_node, trie_row_ptr, trie_code,
                      trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
 }
 

@@ -77,6 +77,8 @@ struct SelArgs {
   const float* logprobs;
   const float* noise;       // [sumW][C] Gumbel draws of the sampled selection, or NULL
   float temp;               // its temperature (>= 0)
+  float* row_lse;           // [sumW] row lse when logprobs holds raw logits, else NULL
+  int32_t lse_ready;        // 1: row_lse is filled before the select kernels run
   const float* scores;
   const int32_t* nodes;
   const int32_t* row_ptr;   // NULL: unconstrained

@@ -351,6 +351,56 @@ __device__ __forceinline__ uint64_t candidate(float s, float lp, float tg, uint3
   return composite_key(ordered_key(ok), flat);
 }
 
+// Selection from raw logits (the fused log-softmax): the log-softmax of a row of C logits
+// is lp = fl32(x - lse) with lse = fl32(ln sum exp(x)) over the whole row, the sum taken in
+// float64 after subtracting the row max.  Every row's lse is computed once, by one
+// workgroup, and kept in row_lse for the kernels that read the row again.
+//
+// lse of the row whose values the NT threads hold in v (-inf outside the row), with the
+// precondition flag for NaN or +inf logits.  redf holds NT / 64 floats, redd NT / 64 doubles.
+template <int NT, int N>
+__device__ __forceinline__ float block_lse(const float (&v)[N], float* redf, double* redd, int& fl) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float m = -INFINITY;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    bad |= __builtin_isnan(v[k]) || v[k] == INFINITY;
+    m = fmaxf(m, v[k]);
+  }
+  if (bad) fl |= GRW_FLAG_NAN_LOGPROB;
+  m = wave_max(m);
+  __syncthreads();
+  if (lane == 0) redf[wave] = m;
+  __syncthreads();
+  m = redf[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, redf[w]);
+  double sum = 0.0;
+  const double md = (double)m;
+#pragma unroll
+  for (int k = 0; k < N; ++k) sum += exp((double)v[k] - md);    // exp(-inf) = 0
+  sum = wave_sum(sum);
+  if (lane == 0) redd[wave] = sum;
+  __syncthreads();
+  sum = redd[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) sum += redd[w];
+  return (float)(md + log(sum));
+}
+
+// lse of a full row of C logits read with stride 256 (rows of at most kOnePass codes).
+__device__ __forceinline__ float row_lse_strided(const float* xrow, int C, float* redf, double* redd, int& fl) {
+  float v[kRegC];
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) {
+    const int i = (int)threadIdx.x + 256 * k;
+    v[k] = i < C ? xrow[i] : -INFINITY;
+  }
+  return block_lse<256, kRegC>(v, redf, redd, fl);
+}
+
 // Row layouts of the one-read path: kFull — all C codes with C % 4 == 0 and an aligned row,
 // thread t holding codes 4 (t + 256 q) + e so that every load is a full 1 KB wave line;
 // kFullScalar — all C codes, thread t holding codes t + 256 k; kTrie — a CSR trie row,
@@ -429,6 +479,25 @@ __device__ __forceinline__ void load_row(RowRegs<L, G>& rr, const SelArgs& a, co
   }
 }
 
+// Raw logits loaded into rr.lp -> log-probabilities: the row's lse is computed here (from
+// the registers when they hold the whole row, else from a strided pass over it) and stored
+// in row_lse, or, when another kernel already computed it, read from row_lse.  Reached by
+// every thread of the workgroup.
+template <int L, bool G>
+__device__ __forceinline__ void to_logprobs(RowRegs<L, G>& rr, const SelArgs& a, int slot, const float* xrow,
+                                            bool compute, float* redf, double* redd, int& fl) {
+  float lse;
+  if (compute) {
+    if constexpr (L == kTrie) lse = row_lse_strided(xrow, a.C, redf, redd, fl);
+    else lse = block_lse<256, kRegC>(rr.lp, redf, redd, fl);
+    if (threadIdx.x == 0) a.row_lse[slot] = lse;
+  } else {
+    lse = a.row_lse[slot];
+  }
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) rr.lp[k] = rr.lp[k] - lse;     // -inf stays -inf
+}
+
 // Ordered key of candidate k of a loaded row (0 when it is not a candidate or is below
 // tau), with the precondition flags.
 template <int L, bool G>
@@ -446,11 +515,13 @@ __device__ __forceinline__ uint32_t row_key(const RowRegs<L, G>& rr, int k, int 
 }
 
 // The best candidate of a row of up to kOnePass candidates (0 when none).
-template <int L, bool G>
-__device__ __forceinline__ uint64_t row_best(const SelArgs& a, const float* lprow, const float* grow,
-                                             const int32_t* codes, int cnt, float s, uint32_t flat_base, int& fl) {
+template <int L, bool G, bool X>
+__device__ __forceinline__ uint64_t row_best(const SelArgs& a, int slot, const float* lprow, const float* grow,
+                                             const int32_t* codes, int cnt, float s, uint32_t flat_base, int& fl,
+                                             float* redf, double* redd) {
   RowRegs<L, G> rr;
   load_row<L, G>(rr, a, lprow, grow, codes, cnt, fl);
+  if constexpr (X) to_logprobs<L, G>(rr, a, slot, lprow, a.lse_ready == 0, redf, redd, fl);
   uint64_t best = 0;
 #pragma unroll
   for (int k = 0; k < kRegC; ++k) {
@@ -499,9 +570,11 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 // top_k of its beam) with device-coherent stores and counts itself; the request's last
 // pilot sets bound[r] to the W_r-th best key of all contributions (0 when there are fewer
 // than W_r) and resets the count.
-template <bool G>
+template <bool G, bool X>
 __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   __shared__ uint64_t red64[4];
+  __shared__ float redf[4];
+  __shared__ double redd[4];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t scr[4];
   __shared__ uint32_t red32[8];
@@ -521,15 +594,18 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes)) {
     if (cnt <= kOnePass) {
       const int lay = row_layout(a, codes, lprow);
-      if (lay == kFull) best = row_best<kFull, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
-      else if (lay == kFullScalar) best = row_best<kFullScalar, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
-      else best = row_best<kTrie, G>(a, lprow, grow, codes, cnt, s, flat_base, fl);
+      if (lay == kFull) best = row_best<kFull, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
+      else if (lay == kFullScalar)
+        best = row_best<kFullScalar, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
+      else best = row_best<kTrie, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
     } else {
+      const float lse = X ? a.row_lse[slot] : 0.0f;    // long rows: computed by select_lse_kernel
       for (int q = tid; q < cnt; q += 256) {
         const int c = codes ? codes[q] : q;
         if ((unsigned)c >= (unsigned)a.C) continue;
         const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
-        best = max(best, candidate<G>(s, lprow[c], tg, flat_base + (uint32_t)c, fl));
+        const float lp = X ? lprow[c] - lse : lprow[c];
+        best = max(best, candidate<G>(s, lp, tg, flat_base + (uint32_t)c, fl));
       }
     }
   }
@@ -577,7 +653,7 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
 // --------------------------------------------------------------------------------------
 // Rows of any length (used when C > kOnePass): rows of up to kOnePass candidates in
 // registers as above; longer rows stream through the LDS buffer.
-template <bool G>
+template <bool G, bool X>
 __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
   __shared__ uint64_t buf[kSelCap];
   __shared__ uint32_t hist[256];
@@ -617,12 +693,17 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
       RowRegs<kTrie, G> rr;  // row positions t + 256 k, codes kept (also for the full range)
       if (codes != nullptr) {
         load_row<kTrie, G>(rr, a, lprow, grow, codes, cnt, fl);
+        if constexpr (X) {
+          const float lse = a.row_lse[slot];
+#pragma unroll
+          for (int k = 0; k < kRegC; ++k) rr.lp[k] = rr.lp[k] - lse;
+        }
       } else {
 #pragma unroll
         for (int k = 0; k < kRegC; ++k) {
           const int i = tid + 256 * k;
           rr.code[k] = i < cnt ? i : -1;
-          rr.lp[k] = i < cnt ? lprow[i] : 0.0f;
+          rr.lp[k] = i < cnt ? (X ? lprow[i] - a.row_lse[slot] : lprow[i]) : 0.0f;
           if constexpr (G) rr.tg[k] = i < cnt ? noise_term(a, grow, i, fl) : 0.0f;
         }
       }
@@ -685,7 +766,8 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
             continue;
           }
           const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
-          const uint64_t x = candidate<G>(s, lprow[c], tg, flat_base + (uint32_t)c, fl);
+          const float lp = X ? lprow[c] - a.row_lse[slot] : lprow[c];
+          const uint64_t x = candidate<G>(s, lp, tg, flat_base + (uint32_t)c, fl);
           if (x != 0 && (uint32_t)(x >> 32) >= tau) e[ne++] = x;
         }
       }
@@ -733,6 +815,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
 // Output slot `rank` of the request: token, parent, exact score, trie child.
 // edge: the CSR edge of the entry when the per-beam stage recorded it (its child is node
 // edge + 1), else -1 (the child is then found by a binary search of the parent's row).
+template <bool X>
 __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int rank, uint64_t v, int edge = -1) {
   const int C = a.C;
   const int slot = rd.boff + rank;
@@ -748,7 +831,8 @@ __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int ra
     return;
   }
   const int ps = rd.boff + (int)b;
-  const float score = a.scores[ps] + a.logprobs[(size_t)ps * C + c];
+  const float x = a.logprobs[(size_t)ps * C + c];
+  const float score = a.scores[ps] + (X ? x - a.row_lse[ps] : x);
   int node = -1;
   if (a.row_ptr != nullptr && edge >= 0) {
     node = edge + 1;
@@ -815,7 +899,7 @@ struct FinalLds {
 // every winner its output position.  When a bin holds more than BINCAP entries, a radix
 // select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
 // device-coherent loads (they may come from other workgroups of the same kernel).
-template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP, bool G = false>
+template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP, bool G = false, bool X = false>
 __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L) {
   constexpr bool EDGES = EDGECAP == WINCAP;   // entries carry their CSR edge (trie rows)
   constexpr int BPT = MAXW / NT;     // beams per thread
@@ -990,7 +1074,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
       const int s0 = (int)L.start[b], e0 = (int)L.start[b + 1];
       int rank = s0;
       for (int q = s0; q < e0; ++q) rank += L.win[q] > v;
-      if (rank < nsel) emit(a, rd, rank, v, EDGES ? L.wedge[p] : -1);
+      if (rank < nsel) emit<X>(a, rd, rank, v, EDGES ? L.wedge[p] : -1);
     }
   } else if (nsel > 0) {
     // fallback: radix select of the W-th entry, gather, bitonic sort
@@ -1029,7 +1113,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
         __syncthreads();
       }
     }
-    for (int i = tid; i < nsel; i += NT) emit(a, rd, i, L.win[i]);
+    for (int i = tid; i < nsel; i += NT) emit<X>(a, rd, i, L.win[i]);
   }
   for (int i = nsel + tid; i < W; i += NT) {
     const int slot = rd.boff + i;
@@ -1044,11 +1128,11 @@ constexpr int kGlobThreads = 1024;
 constexpr int kGlobWinCap = kMaxW + kBinCap;
 typedef FinalLds<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, 1> GlobLds;
 
-template <bool G>
+template <bool G, bool X>
 __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GlobLds& L = *(GlobLds*)smem;
-  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G>(a, blockIdx.x, L);
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G, X>(a, blockIdx.x, L);
   if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
 }
 
@@ -1186,7 +1270,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
 // by the NT threads of the request's W-of-pool workgroup: the row is read again, NR
 // positions per thread (rows of at most NT * NR candidates), a radix select finds the
 // top_k-th composite, and the survivors go to the beam's pool region.
-template <int NT, int NR, bool G>
+template <int NT, int NR, bool G, bool X>
 __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd, int r, int slot, uint32_t* hist,
                                              uint32_t* scr, uint32_t* red32, int* red) {
   const int tid = threadIdx.x;
@@ -1214,6 +1298,7 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
     code[k] = i < cnt ? (codes != nullptr ? codes[i] : i) : -1;
     if ((unsigned)code[k] >= (unsigned)a.C) code[k] = -1;
     lp[k] = code[k] >= 0 ? lprow[code[k]] : -INFINITY;
+    if constexpr (X) lp[k] = lp[k] - a.row_lse[slot];
     if constexpr (G) tg[k] = code[k] >= 0 ? noise_term(a, grow, code[k], fl) : 0.0f;
     na += order_key<G>(s + lp[k], G ? tg[k] : 0.0f) >= tau_f;
   }
@@ -1250,9 +1335,11 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
 // Per-beam stage: survivors of each beam slot (candidates >= the request's bound) into the
 // slot's pool region, and the slot's survivor count (-1: more than top_k without noise,
 // left to the W-of-pool stage).
-template <int L, bool G>
+template <int L, bool G, bool X>
 __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   __shared__ int red[4];
+  __shared__ float redf[X ? 4 : 1];
+  __shared__ double redd[X ? 4 : 1];
   __shared__ uint32_t hist[G ? 256 : 1];
   __shared__ uint32_t scr[4];
   __shared__ uint32_t red32[8];
@@ -1262,6 +1349,11 @@ __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   const BeamRow b = beam_setup(a, slot, fl);
   RowRegs<L, G> rr;
   if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl);
+  if constexpr (X) {
+    // pilot slots' lse came from the pilot kernel; the others are computed here
+    const bool pilot = b.slot - b.rd.boff < (G ? b.rd.n_pilot_s : b.rd.n_pilot);
+    if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, !pilot, redf, redd, fl);
+  }
   const int n_out = keep_beam<L, G>(a, b, rr, fl, red, hist, scr, red32);
   if (tid == 0) a.surv_count[slot] = n_out;
 #pragma unroll
@@ -1274,7 +1366,7 @@ __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
 constexpr int kFinThreads = 1024;
 typedef FinalLds<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedWinCap> FinLds;
 
-template <bool G>
+template <bool G, bool X>
 __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   FinLds& L = *(FinLds*)smem;
@@ -1293,13 +1385,46 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   for (int i = 0; i < no; ++i) {
     const int slot = (int)L.pre[i];
     __syncthreads();
-    overflow_row<kFinThreads, kOnePass / kFinThreads, G>(a, rd, r, slot, L.hist, L.scr, red32, red);
+    overflow_row<kFinThreads, kOnePass / kFinThreads, G, X>(a, rd, r, slot, L.hist, L.scr, red32, red);
   }
   wait_stores();
   __syncthreads();
-  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G>(a, r, L);
+  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, L);
   __syncthreads();
   if (threadIdx.x == 0) a.bound[r] = 0u;
+}
+
+// Row lse of every live beam slot for the general kernels (rows of any length, read with
+// stride 256 twice: max, then the float64 sum of exp(x - max)).
+__global__ __launch_bounds__(256) void select_lse_kernel(SelArgs a) {
+  __shared__ float redf[4];
+  __shared__ double redd[4];
+  const int slot = blockIdx.x;
+  const float s = a.scores[slot];
+  if (s == -INFINITY || __builtin_isnan(s)) return;
+  const float* xrow = a.logprobs + (size_t)slot * a.C;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int fl = 0;
+  float m = -INFINITY;
+  for (int i = threadIdx.x; i < a.C; i += 256) {
+    const float x = xrow[i];
+    if (__builtin_isnan(x) || x == INFINITY) fl |= GRW_FLAG_NAN_LOGPROB;
+    m = fmaxf(m, x);
+  }
+  m = wave_max(m);
+  if (lane == 0) redf[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+  const double md = (double)m;
+  double sum = 0.0;
+  for (int i = threadIdx.x; i < a.C; i += 256) sum += exp((double)xrow[i] - md);
+  sum = wave_sum(sum);
+  if (lane == 0) redd[wave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) a.row_lse[slot] = (float)(md + log(((redd[0] + redd[1]) + redd[2]) + redd[3]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  if (lane == 0 && fl) atomicOr(a.flags, fl);
 }
 
 __global__ void beams_init_kernel(const ReqDesc* req, const int32_t* slot_req, int sumW,
@@ -1339,63 +1464,70 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 }  // namespace
 
-template <bool G>
+template <bool G, bool X>
 hipError_t select_topk_path(const SelArgs& a, hipStream_t s) {
-  select_pilot_kernel<G><<<a.n_pilots, 256, 0, s>>>(a);
-  select_topk_kernel<G><<<a.sumW, 256, 0, s>>>(a);
+  if (X) select_lse_kernel<<<a.sumW, 256, 0, s>>>(a);
+  select_pilot_kernel<G, X><<<a.n_pilots, 256, 0, s>>>(a);
+  select_topk_kernel<G, X><<<a.sumW, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_topk(const SelArgs& a, hipStream_t s) {
   if (a.sumW == 0) return hipSuccess;
-  return a.noise != nullptr ? select_topk_path<true>(a, s) : select_topk_path<false>(a, s);
+  const bool g = a.noise != nullptr, x = a.row_lse != nullptr;
+  if (g) return x ? select_topk_path<true, true>(a, s) : select_topk_path<true, false>(a, s);
+  return x ? select_topk_path<false, true>(a, s) : select_topk_path<false, false>(a, s);
 }
 
-template <bool G>
+template <bool G, bool X>
 hipError_t select_global_path(const SelArgs& a, hipStream_t s) {
   static bool attr_set = false;   // the bin arrays and winner array exceed the default 64 KB
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_global_kernel<G>,
+    hipError_t e = hipFuncSetAttribute((const void*)select_global_kernel<G, X>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GlobLds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  select_global_kernel<G><<<a.R, kGlobThreads, sizeof(GlobLds), s>>>(a);
+  select_global_kernel<G, X><<<a.R, kGlobThreads, sizeof(GlobLds), s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_global(const SelArgs& a, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  return a.noise != nullptr ? select_global_path<true>(a, s) : select_global_path<false>(a, s);
+  const bool g = a.noise != nullptr, x = a.row_lse != nullptr;
+  if (g) return x ? select_global_path<true, true>(a, s) : select_global_path<true, false>(a, s);
+  return x ? select_global_path<false, true>(a, s) : select_global_path<false, false>(a, s);
 }
 
 bool select_fused_ok(int C, int max_W) { return C <= kOnePass && max_W <= kFusedMaxW; }
 
-template <bool G>
+template <bool G, bool X>
 hipError_t select_fused_path(const SelArgs& a, hipStream_t s) {
   static bool attr_set = false;   // the W-of-pool select's arrays exceed the default 64 KB
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_final_kernel<G>,
+    hipError_t e = hipFuncSetAttribute((const void*)select_final_kernel<G, X>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FinLds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  select_pilot_kernel<G><<<a.n_pilots, 256, 0, s>>>(a);
+  select_pilot_kernel<G, X><<<a.n_pilots, 256, 0, s>>>(a);
   const int grid = a.sumW;
   const bool aligned = (((uintptr_t)a.logprobs) & 15) == 0 && (!G || (((uintptr_t)a.noise) & 15) == 0);
   if (a.row_ptr != nullptr)
-    select_beam_kernel<kTrie, G><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kTrie, G, X><<<grid, 256, 0, s>>>(a);
   else if ((a.C & 3) == 0 && aligned)
-    select_beam_kernel<kFull, G><<<grid, 256, 0, s>>>(a);
+    select_beam_kernel<kFull, G, X><<<grid, 256, 0, s>>>(a);
   else
-    select_beam_kernel<kFullScalar, G><<<grid, 256, 0, s>>>(a);
-  select_final_kernel<G><<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
+    select_beam_kernel<kFullScalar, G, X><<<grid, 256, 0, s>>>(a);
+  select_final_kernel<G, X><<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_select_fused(const SelArgs& a, hipStream_t s) {
   if (a.sumW == 0) return hipSuccess;
-  return a.noise != nullptr ? select_fused_path<true>(a, s) : select_fused_path<false>(a, s);
+  const bool g = a.noise != nullptr, x = a.row_lse != nullptr;
+  if (g) return x ? select_fused_path<true, true>(a, s) : select_fused_path<true, false>(a, s);
+  return x ? select_fused_path<false, true>(a, s) : select_fused_path<false, false>(a, s);
 }
 
 hipError_t launch_beams_init(const ReqDesc* req, const int32_t* slot_req, int32_t sumW,

@@ -29,12 +29,18 @@ class DecodeLoop:
         self.parents = torch.empty(S, sumW, dtype=torch.int32, device=dev)   # parent_idx
         self.sid = torch.empty(sumW, S, dtype=torch.int32, device=dev)
 
-    def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0):
-        """Selection at depth d; with noise, the Gumbel top-k at the given temperature."""
-        from . import beam_select, beam_select_gumbel
+    def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0,
+                    raw_logits: bool = False):
+        """Selection at depth d; with noise, the Gumbel top-k at the given temperature; with
+        raw_logits, `logprobs` holds raw logits and the row log-softmax is fused in."""
+        from . import beam_select, beam_select_gumbel, beam_select_logits
         cur, nxt = d % 2, (d + 1) % 2
         row_ptr, code, n_int = self.trie if self.trie is not None else (None, None, 0)
-        if noise is None:
+        if raw_logits:
+            beam_select_logits(self.ws, logprobs, noise, temperature, self.scores[cur], self.nodes[cur],
+                               row_ptr, code, n_int, self.W, self.K, self.C, self.tokens[d], self.parents[d],
+                               self.scores[nxt], self.nodes[nxt], stream)
+        elif noise is None:
             beam_select(self.ws, logprobs, self.scores[cur], self.nodes[cur], row_ptr, code, n_int,
                         self.W, self.K, self.C, self.tokens[d], self.parents[d], self.scores[nxt],
                         self.nodes[nxt], stream)
@@ -48,17 +54,19 @@ class DecodeLoop:
         beam_attn_decode(self.ws, layer["q"][d], layer["k_s"], layer["v_s"], layer.get("k_scale"),
                          layer.get("v_scale"), layer["k_u"], layer["v_u"], self.parents, d, out, stream)
 
-    def run(self, logprobs, layers, out, stream=None, steps=None, noise=None, temperature: float = 0.0):
+    def run(self, logprobs, layers, out, stream=None, steps=None, noise=None, temperature: float = 0.0,
+            raw_logits: bool = False):
         """logprobs: sequence of S device tensors [sumW][C]; layers: sequence of dicts with
         q [S][sumW][Hq][D], k_s, v_s, k_scale, v_scale, k_u, v_u (device tensors);
         out: [sumW][Hq][D] float32 device tensor, or a list with one per layer;
         noise: None, or a sequence of S device tensors [sumW][C] of Gumbel draws for the
-        sampled selection at the given temperature."""
+        sampled selection at the given temperature; raw_logits: logprobs holds raw logits
+        and the selection fuses their log-softmax."""
         from . import grw_backtrack
         steps = self.S if steps is None else steps
         self.ws.beams_init(self.scores[0], self.nodes[0], stream)
         for d in range(steps):
-            self.select_step(d, logprobs[d], stream, None if noise is None else noise[d], temperature)
+            self.select_step(d, logprobs[d], stream, None if noise is None else noise[d], temperature, raw_logits)
             for li, layer in enumerate(layers):
                 self.attn_step(d, layer, out[li] if isinstance(out, (list, tuple)) else out, stream)
         if steps == self.S:

@@ -4,6 +4,7 @@
  * One decode step of wide-beam generative recommendation:
  *   beam_select       trie-masked per-beam top_k, then the global beam_width-of-pool select
  *   beam_select_gumbel the same with Gumbel-perturbed ordering keys (temperature > 0)
+ *   beam_select_logits the same from raw logits, with the row log-softmax fused in
  *   beam_attn_decode  beam attention over a shared prompt KV plus per-beam decode KV
  *                     reached through parent pointers, in three stages
  *                     (shared stage, unshared stage, online-softmax merge)
@@ -232,6 +233,33 @@ int beam_select(grw_ws* ws, const float* logprobs, const float* beam_scores,
  *   other arguments as for beam_select
  */
 int beam_select_gumbel(grw_ws* ws, const float* logprobs, const float* noise, float temperature,
+                       const float* beam_scores, const int32_t* beam_node,
+                       const int32_t* trie_row_ptr, const int32_t* trie_code,
+                       int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
+                       int32_t* out_token, int32_t* out_parent, float* out_score,
+                       int32_t* out_node, void* stream);
+
+/*
+ * beam_select_logits — the selection step from raw logits, with the log-softmax fused in
+ * (the step upstream of the selection in the xLLM design doc's device loop, section 6:
+ * forward, then sampling and beam search on the device).  Saves writing the log-probability
+ * rows and reading them back.
+ *
+ * For every live slot b the log-softmax over all C codes of its row is taken first:
+ *   lse_b = fl32(ln sum_c exp(logits[b][c])), evaluated in float64 as m + ln sum exp(x - m)
+ *           with m the row max, rounded once;
+ *   lp(b, c) = fl32(logits[b][c] - lse_b), one float32 subtraction;
+ * then the selection proceeds exactly as beam_select on lp (or as beam_select_gumbel when
+ * noise is not NULL).  lp <= 0 holds by construction, so the early exit is always valid.
+ * Every row's lse is computed once, by one workgroup, into the workspace.
+ *
+ *   logits       [sumW][C] float32, row-major; finite or -inf, at least one finite logit in
+ *                every live row (NaN or +inf raise GRW_FLAG_NAN_LOGPROB)
+ *   noise        NULL for the deterministic selection, else as for beam_select_gumbel
+ *   temperature  used with noise only: finite, >= 0 (else GRW_EINVAL, nothing enqueued)
+ *   other arguments as for beam_select; out_score is beam_scores[b] + lp(b, c)
+ */
+int beam_select_logits(grw_ws* ws, const float* logits, const float* noise, float temperature,
                        const float* beam_scores, const int32_t* beam_node,
                        const int32_t* trie_row_ptr, const int32_t* trie_code,
                        int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,

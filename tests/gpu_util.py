@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 from oracle.attention import oracle_attention
-from oracle.select import catalog_prefix_sets, initial_beams, oracle_select
+from oracle.select import catalog_prefix_sets, initial_beams, oracle_select, oracle_select_logits
 from synth import build_trie_csr
 
 
@@ -34,10 +34,11 @@ def trie_device(trie):
 
 
 def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
-                          noise_of_step=None, temperature=0.0):
+                          noise_of_step=None, temperature=0.0, raw_logits=False):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
     every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
-    the steps are the Gumbel-sampled selection at the given temperature.  Returns the loop."""
+    the steps are the Gumbel-sampled selection at the given temperature; with raw_logits,
+    lp_of_step returns raw logits and the steps fuse their log-softmax.  Returns the loop."""
     Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
     R = len(Ws)
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
@@ -54,7 +55,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
         g = noise_of_step(d) if noise_of_step is not None else None
         loop.select_step(d, torch.from_numpy(np.ascontiguousarray(lp)).cuda(),
                          noise=None if g is None else torch.from_numpy(np.ascontiguousarray(g)).cuda(),
-                         temperature=temperature)
+                         temperature=temperature, raw_logits=raw_logits)
         torch.cuda.synchronize()
         tok = loop.tokens[d].cpu().numpy()
         par = loop.parents[d].cpu().numpy()
@@ -63,8 +64,9 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
         for r in check:
             a, W = boff[r], Ws[r]
             scores, prefixes = state[r]
-            res = oracle_select(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets,
-                                None if g is None else g[a:a + W], temperature)
+            sel = oracle_select_logits if raw_logits else oracle_select
+            res = sel(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets,
+                      None if g is None else g[a:a + W], temperature)
             where = f"{label} step {d} request {r}"
             np.testing.assert_array_equal(tok[a:a + W], res["tokens"], err_msg=where + " tokens")
             np.testing.assert_array_equal(par[a:a + W], res["parents"], err_msg=where + " parents")

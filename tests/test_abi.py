@@ -28,7 +28,8 @@ def clib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("beam_attn_decode", "beam_select", "beam_select_gumbel", "grw_ws_create", "grw_ws_destroy",
+    for n in ("beam_attn_decode", "beam_select", "beam_select_gumbel", "beam_select_logits", "grw_ws_create",
+              "grw_ws_destroy",
               "grw_ws_bind_batch", "grw_beams_init", "grw_backtrack", "grw_ws_error",
               "grw_ws_splits", "grw_ws_pool_size", "grw_status_str"):
         assert n in names
@@ -75,5 +76,9 @@ def test_null_handles_rejected(clib):
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 4 + \
         [ctypes.c_void_p] * 5
     assert f(None, None, None, 1.0, None, None, None, None, 0, 1, 1, 1, None, None, None, None, None) == 1
+    f = clib.beam_select_logits
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 4 + \
+        [ctypes.c_void_p] * 5
+    assert f(None, None, None, 0.0, None, None, None, None, 0, 1, 1, 1, None, None, None, None, None) == 1
     assert clib.grw_backtrack(None, None, None, 1, None, None) == 1
     assert clib.grw_ws_pool_size(None, 0, None, None) == 1
