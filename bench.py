@@ -185,6 +185,68 @@ def stage_timings(wl, st, reps):
     return res
 
 
+def dense_sweep(seed, dev, reps=10):
+    """The wide512 3-step select loop (Zipf trie) with a CSR-only trie and with dense child
+    masks for the nodes of at least `threshold` children: device time per loop (HIP graph of
+    `reps` loops, best of 5 replays), and whether the outputs equal the CSR-only ones."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    from synth import build_trie_csr, catalog_items, request_shapes, workload
+    wl = workload("wide512")
+    W, K, P = request_shapes(wl, seed)
+    sumW, C, S = int(W.sum()), wl.C, wl.S
+    g = torch.Generator(device=dev).manual_seed(seed)
+    lps = []
+    for _ in range(S):
+        x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
+        lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
+        del x
+    t = build_trie_csr(catalog_items(wl, seed), C)
+    base = (torch.from_numpy(t["row_ptr"]).to(dev), torch.from_numpy(t["code"]).to(dev), t["n_internal"])
+    fan = np.diff(t["row_ptr"][: t["n_internal"] + 1])
+    ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
+                       max_C=C, max_S=S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                       q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
+    ws.bind_batch(W, K, P)
+    rows, ref = [], None
+    for thr in (None, 4096, 1024, 256):
+        trie = base
+        if thr is not None:
+            slot, masks = grw.trie_dense_build(t["row_ptr"], t["code"], t["n_internal"], C, thr)
+            trie = base + (torch.from_numpy(slot).to(dev), torch.from_numpy(masks.view(np.int32)).to(dev))
+        loop = grw.DecodeLoop(ws, S, C, trie, device=dev)
+
+        def run():
+            ws.beams_init(loop.scores[0], loop.nodes[0])
+            for d in range(S):
+                loop.select_step(d, lps[d])
+        run()
+        torch.cuda.synchronize()
+        out = (loop.tokens.clone(), loop.parents.clone(), loop.final_scores().view(torch.int32).clone())
+        ref = out if ref is None else ref
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(5):
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        del graph
+        rows.append({"min_fanout": thr, "dense_nodes": int((fan >= thr).sum()) if thr else 0,
+                     "us_per_3step_loop": round(min(ts) * 1e3, 1),
+                     "equal_to_csr": bool(all(torch.equal(a, b) for a, b in zip(out, ref)))})
+    flags = ws.error_flags()
+    ws.close()
+    return {"workload": "wide512", "select_loops": rows, "device_flags": flags}
+
+
 def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
     """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
     262144-entry pools): device time of one call with every beam live (the third decode step,
@@ -463,6 +525,8 @@ def main():
                     help="with --select-only: time beam_select_gumbel at this temperature")
     ap.add_argument("--select-logits", action="store_true",
                     help="with --select-only: time beam_select_logits on raw logits")
+    ap.add_argument("--dense-sweep", action="store_true",
+                    help="time the wide512 select loop with dense child masks at several fan-out thresholds")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -487,6 +551,9 @@ def main():
     wl = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dense_sweep:
+        print(json.dumps(dense_sweep(args.seed, dev)), flush=True)
+        return 0
     if args.select_only:
         print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature,
                                          raw_logits=args.select_logits)), flush=True)

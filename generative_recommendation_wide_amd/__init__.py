@@ -159,6 +159,42 @@ def beam_select_logits(ws: Workspace, logits, noise, temperature: float, beam_sc
         _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
 
 
+def beam_select_ex(ws: Workspace, input, beam_scores, beam_node, trie, W: int, K: int, C: int, out_token,
+                   out_parent, out_score, out_node, noise=None, temperature: float = 0.0, raw_logits: bool = False,
+                   stream=None):
+    """The selection step with every option (see include/grw.h).  trie: None, or a tuple
+    (row_ptr, code, n_internal) or (row_ptr, code, n_internal, dense_slot, dense_mask) of
+    device tensors (n_internal an int)."""
+    t = None
+    if trie is not None:
+        row_ptr, code, n_int = trie[:3]
+        dslot, dmask = (trie[3], trie[4]) if len(trie) > 3 else (None, None)
+        t = _lib.GrwTrie(_ptr(row_ptr, _I32, "row_ptr"), _ptr(code, _I32, "code"), int(n_int),
+                         _ptr(dslot, _I32, "dense_slot"), _ptr(dmask, (torch.int32, torch.uint32), "dense_mask"))
+    o = _lib.GrwSelectOpts(_ptr(noise, _F32, "noise"), float(temperature), int(bool(raw_logits)))
+    _lib.check("beam_select_ex", _L.beam_select_ex(
+        ws.handle, _ptr(input, _F32, "input"), _ptr(beam_scores, _F32, "beam_scores"),
+        _ptr(beam_node, _I32, "beam_node"), ctypes.byref(t) if t is not None else None, ctypes.byref(o),
+        int(W), int(K), int(C), _ptr(out_token, _I32, "out_token"), _ptr(out_parent, _I32, "out_parent"),
+        _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
+
+
+def trie_dense_build(row_ptr, code, n_internal: int, C: int, min_fanout: int):
+    """Host-side dense child masks (see grw_trie_dense_build): numpy int32 CSR arrays in,
+    numpy (dense_slot int32 [n_internal], dense_mask uint32 [n_dense][(C + 31) // 32]) out."""
+    import numpy as np
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    code = np.ascontiguousarray(code, dtype=np.int32)
+    slot = np.empty(int(n_internal), np.int32)
+    n = ctypes.c_int32(0)
+    args = (row_ptr.ctypes.data, code.ctypes.data, int(n_internal), int(C), int(min_fanout), slot.ctypes.data)
+    _lib.check("grw_trie_dense_build", _L.grw_trie_dense_build(*args, None, ctypes.byref(n)))
+    masks = np.empty((n.value, (int(C) + 31) // 32), np.uint32)
+    _lib.check("grw_trie_dense_build", _L.grw_trie_dense_build(*args, masks.ctypes.data if n.value else None,
+                                                               ctypes.byref(n)))
+    return slot, masks
+
+
 def grw_backtrack(ws: Workspace, tokens, parents, S: int, sid_out, stream=None):
     """Semantic-ID tuples [sumW][S] of the final beams (see include/grw.h)."""
     _lib.check("grw_backtrack", _L.grw_backtrack(

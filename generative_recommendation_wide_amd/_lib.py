@@ -20,14 +20,24 @@ FLAG_BAD_NOISE = 64
 STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
-            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "beam_select_gumbel", "beam_select_logits", "grw_backtrack", "grw_ws_error", "grw_ws_splits",
-            "grw_ws_pool_size", "grw_status_str"]
+            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "beam_select_gumbel",
+            "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_backtrack", "grw_ws_error",
+            "grw_ws_splits", "grw_ws_pool_size", "grw_status_str"]
 
 
 class GrwLimits(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "max_requests", "max_total_beams", "max_W", "max_K", "max_C", "max_S", "max_P",
         "Hq", "Hkv", "D", "q_dtype", "kv_dtype", "max_splits")]
+
+
+class GrwTrie(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("code", ctypes.c_void_p), ("n_internal", ctypes.c_int32),
+                ("dense_slot", ctypes.c_void_p), ("dense_mask", ctypes.c_void_p)]
+
+
+class GrwSelectOpts(ctypes.Structure):
+    _fields_ = [("noise", ctypes.c_void_p), ("temperature", ctypes.c_float), ("raw_logits", ctypes.c_int32)]
 
 
 class GrwError(RuntimeError):
@@ -61,6 +71,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                i32p, vp],
         "beam_select_logits": [vp, fp, fp, ctypes.c_float, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp,
                                i32p, vp],
+        "beam_select_ex": [vp, fp, fp, i32p, ctypes.POINTER(GrwTrie), ctypes.POINTER(GrwSelectOpts), i32, i32, i32,
+                           i32p, i32p, fp, i32p, vp],
+        "grw_trie_dense_build": [vp, vp, i32, i32, i32, vp, vp, ctypes.POINTER(i32)],
         "grw_backtrack": [vp, i32p, i32p, i32, i32p, vp],
         "grw_ws_error": [vp, vp, ctypes.POINTER(i32)],
         "grw_ws_splits": [vp, i32, ctypes.POINTER(i32)],

@@ -474,7 +474,8 @@ namespace {
 int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* noise, float temperature,
                 const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
                 const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
-                int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream) {
+                int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream,
+                const int32_t* dense_slot = nullptr, const uint32_t* dense_mask = nullptr) {
   if (!w) return GRW_EINVAL;
   if (!w->bound) return GRW_ESTATE;
   const grw_limits& L = w->lim;
@@ -487,6 +488,7 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   if ((uint64_t)w->maxW * (uint64_t)C >= (1ull << 32)) return GRW_EUNSUPPORTED;
   if ((const void*)out_score == (const void*)beam_scores || (const void*)out_node == (const void*)beam_node)
     return GRW_EINVAL;
+  if ((dense_slot != nullptr) != (dense_mask != nullptr) || (dense_slot && !trie)) return GRW_EINVAL;
   SelArgs a{};
   a.req = w->d_req;
   a.slot_req = w->d_slot_req;
@@ -500,6 +502,9 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   a.row_ptr = trie ? trie_row_ptr : nullptr;
   a.code = trie ? trie_code : nullptr;
   a.n_internal = trie_n_internal;
+  a.dense_slot = trie ? dense_slot : nullptr;
+  a.dense_mask = trie ? dense_mask : nullptr;
+  a.mask_words = (C + 31) / 32;
   a.C = C;
   a.sumW = w->sumW;
   a.R = w->R;
@@ -535,6 +540,45 @@ int beam_select(grw_ws* w, const float* logprobs, const float* beam_scores, cons
                 float* out_score, int32_t* out_node, void* stream) {
   return select_step(w, logprobs, false, nullptr, 0.0f, beam_scores, beam_node, trie_row_ptr, trie_code,
                      trie_n_internal, W, K, C, out_token, out_parent, out_score, out_node, stream);
+}
+
+int beam_select_ex(grw_ws* w, const float* input, const float* beam_scores, const int32_t* beam_node,
+                   const grw_trie* trie, const grw_select_opts* opts, int32_t W, int32_t K, int32_t C,
+                   int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream) {
+  const float* noise = opts ? opts->noise : nullptr;
+  const float temperature = opts ? opts->temperature : 0.0f;
+  if (opts && opts->raw_logits != 0 && opts->raw_logits != 1) return GRW_EINVAL;
+  if (noise && (!(temperature >= 0.0f) || !std::isfinite(temperature))) return GRW_EINVAL;
+  return select_step(w, input, opts && opts->raw_logits, noise, temperature, beam_scores, beam_node,
+                     trie ? trie->row_ptr : nullptr, trie ? trie->code : nullptr, trie ? trie->n_internal : 0,
+                     W, K, C, out_token, out_parent, out_score, out_node, stream,
+                     trie ? trie->dense_slot : nullptr, trie ? trie->dense_mask : nullptr);
+}
+
+int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_internal, int32_t C,
+                         int32_t min_fanout, int32_t* dense_slot, uint32_t* dense_mask, int32_t* n_dense) {
+  if (!row_ptr || !code || !dense_slot || !n_dense || n_internal < 1 || C < 1 || min_fanout < 1)
+    return GRW_EINVAL;
+  const int64_t words = (C + 31) / 32;
+  int32_t n = 0;
+  for (int32_t v = 0; v < n_internal; ++v) {
+    const int64_t beg = row_ptr[v], end = row_ptr[v + 1];
+    if (beg < 0 || end < beg) return GRW_EINVAL;
+    dense_slot[v] = end - beg >= min_fanout ? n++ : -1;
+  }
+  *n_dense = n;
+  if (!dense_mask) return GRW_OK;   // count only
+  std::memset(dense_mask, 0, sizeof(uint32_t) * words * n);
+  for (int32_t v = 0; v < n_internal; ++v) {
+    if (dense_slot[v] < 0) continue;
+    uint32_t* m = dense_mask + words * dense_slot[v];
+    for (int64_t e = row_ptr[v]; e < row_ptr[v + 1]; ++e) {
+      const int32_t c = code[e];
+      if (c < 0 || c >= C) return GRW_EINVAL;
+      m[c >> 5] |= 1u << (c & 31);
+    }
+  }
+  return GRW_OK;
 }
 
 int beam_select_logits(grw_ws* w, const float* logits, const float* noise, float temperature,

@@ -307,17 +307,24 @@ __device__ __forceinline__ int block_compact_ge(uint64_t* buf, int n, uint64_t T
   return *counter;
 }
 
-// The candidates of a beam slot: its CSR trie row (or all C codes).  Returns false when
-// the node is out of range.
-__device__ __forceinline__ bool beam_row(const SelArgs& a, int slot, int& cnt, const int32_t*& codes) {
+// The candidates of a beam slot: its CSR trie row (or all C codes), and the node's dense
+// child bit mask when the trie has one for it (FlashRec announcement: the SID trie is dense
+// or CSR).  Returns false when the node is out of range.
+__device__ __forceinline__ bool beam_row(const SelArgs& a, int slot, int& cnt, const int32_t*& codes,
+                                         const uint32_t** mask = nullptr) {
   cnt = a.C;
   codes = nullptr;
+  if (mask) *mask = nullptr;
   if (a.row_ptr != nullptr) {
     const int node = a.nodes[slot];
     if (node < 0 || node >= a.n_internal) return false;
     const int beg = a.row_ptr[node];
     cnt = a.row_ptr[node + 1] - beg;
     codes = a.code + beg;
+    if (mask && a.dense_slot != nullptr) {
+      const int ds = a.dense_slot[node];
+      if (ds >= 0) *mask = a.dense_mask + (size_t)ds * a.mask_words;
+    }
   }
   return true;
 }
@@ -428,8 +435,24 @@ struct RowRegs {
 // candidate read as -inf.
 template <int L, bool G = false>
 __device__ __forceinline__ void load_row(RowRegs<L, G>& rr, const SelArgs& a, const float* lprow,
-                                         const float* grow, const int32_t* codes, int cnt, int& fl) {
+                                         const float* grow, const int32_t* codes, int cnt, int& fl,
+                                         const uint32_t* mask = nullptr) {
   const int tid = threadIdx.x;
+  if constexpr (L == kTrie) {
+    if (mask != nullptr) {
+      // dense row: thread t holds codes t + 256 k, read in full lines; the bit mask keeps the
+      // children (a wave's 64 codes of one k share two mask words)
+#pragma unroll
+      for (int k = 0; k < kRegC; ++k) {
+        const int c = tid + 256 * k;
+        const bool ok = c < a.C && ((mask[c >> 5] >> (c & 31)) & 1u);
+        rr.code[k] = ok ? c : -1;
+        rr.lp[k] = ok ? lprow[c] : -INFINITY;
+        if constexpr (G) rr.tg[k] = ok ? noise_term(a, grow, c, fl) : 0.0f;
+      }
+      return;
+    }
+  }
   if constexpr (L == kFull) {
 #pragma unroll
     for (int q = 0; q < kRegC / 4; ++q) {
@@ -518,9 +541,9 @@ __device__ __forceinline__ uint32_t row_key(const RowRegs<L, G>& rr, int k, int 
 template <int L, bool G, bool X>
 __device__ __forceinline__ uint64_t row_best(const SelArgs& a, int slot, const float* lprow, const float* grow,
                                              const int32_t* codes, int cnt, float s, uint32_t flat_base, int& fl,
-                                             float* redf, double* redd) {
+                                             float* redf, double* redd, const uint32_t* mask = nullptr) {
   RowRegs<L, G> rr;
-  load_row<L, G>(rr, a, lprow, grow, codes, cnt, fl);
+  load_row<L, G>(rr, a, lprow, grow, codes, cnt, fl, mask);
   if constexpr (X) to_logprobs<L, G>(rr, a, slot, lprow, a.lse_ready == 0, redf, redd, fl);
   uint64_t best = 0;
 #pragma unroll
@@ -591,13 +614,14 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   int cnt = a.C, fl = 0;
   const int32_t* codes = nullptr;
   uint64_t best = 0;
-  if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes)) {
+  const uint32_t* mask = nullptr;
+  if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes, &mask)) {
     if (cnt <= kOnePass) {
       const int lay = row_layout(a, codes, lprow);
       if (lay == kFull) best = row_best<kFull, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
       else if (lay == kFullScalar)
         best = row_best<kFullScalar, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
-      else best = row_best<kTrie, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
+      else best = row_best<kTrie, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd, mask);
     } else {
       const float lse = X ? a.row_lse[slot] : 0.0f;    // long rows: computed by select_lse_kernel
       for (int q = tid; q < cnt; q += 256) {
@@ -1156,6 +1180,7 @@ struct BeamRow {
   uint32_t tau;        // the request's bound
   ReqDesc rd;
   const int32_t* codes;
+  const uint32_t* mask;  // dense child mask of the node, or NULL (CSR row)
   const float* lprow;
 };
 
@@ -1168,11 +1193,12 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
   b.tau = a.bound[b.r];
   b.cnt = a.C;
   b.codes = nullptr;
+  b.mask = nullptr;
   b.lprow = a.logprobs + (size_t)slot * a.C;
   b.beg = 0;
   b.live = b.s != -INFINITY && !__builtin_isnan(b.s);
   if (__builtin_isnan(b.s)) fl |= GRW_FLAG_NAN_LOGPROB;
-  if (b.live && !beam_row(a, slot, b.cnt, b.codes)) {
+  if (b.live && !beam_row(a, slot, b.cnt, b.codes, &b.mask)) {
     fl |= GRW_FLAG_BAD_NODE;
     b.live = false;
   }
@@ -1192,7 +1218,8 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
 // Reached by every thread of the workgroup.
 template <int L, bool G>
 __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L, G>& rr, int& fl, int* red,
-                                         uint32_t* hist, uint32_t* scr, uint32_t* red32) {
+                                         uint32_t* hist, uint32_t* scr, uint32_t* red32, uint32_t* mwords,
+                                         uint32_t* mprefix) {
   const ReqDesc& rd = b.rd;
   const uint32_t tau = b.tau;
   // a beam below the bound keeps nothing: no key exceeds its beam's score (with noise an
@@ -1226,6 +1253,27 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   const int K = rd.K;
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
   int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
+  // CSR edge of a survivor: position t + 256 k of a CSR row; in a dense row the rank of its
+  // code among the node's children (popcount of the mask below it)
+  if constexpr (L == kTrie) {
+    if (b.mask != nullptr) {
+      const int w = threadIdx.x;
+      const uint32_t m = w < a.mask_words ? b.mask[w] : 0u;   // mask_words <= 256 on this path
+      mwords[w] = m;
+      int tot;
+      mprefix[w] = (uint32_t)block_excl_scan<256>(__builtin_popcount(m), red, &tot);
+      __syncthreads();
+    }
+  }
+  auto edge_of = [&](int k) -> int {
+    if constexpr (L == kTrie) {
+      if (b.mask == nullptr) return b.beg + (int)threadIdx.x + 256 * k;
+      const int c = rr.code[k];
+      return b.beg + (int)mprefix[c >> 5] + __builtin_popcount(mwords[c >> 5] & ((1u << (c & 31)) - 1u));
+    } else {
+      return -1;
+    }
+  };
   if (n > K) {
     if constexpr (!G) {
       return -1;
@@ -1248,7 +1296,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
 #pragma unroll
       for (int k = 0; k < kRegC; ++k) {
         if ((keep >> k) & 1u) {
-          if constexpr (L == kTrie) redge[q] = b.beg + (int)threadIdx.x + 256 * k;
+          if constexpr (L == kTrie) redge[q] = edge_of(k);
           region[q++] = composite_key(key(k), flat(k));
         }
       }
@@ -1259,7 +1307,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   for (int k = 0; k < kRegC; ++k) {
     const float kf = order_key<G>(b.s + rr.lp[k], G ? rr.tg[k] : 0.0f);
     if (kf >= tau_f) {
-      if constexpr (L == kTrie) redge[p] = b.beg + (int)threadIdx.x + 256 * k;
+      if constexpr (L == kTrie) redge[p] = edge_of(k);
       region[p++] = composite_key(ordered_key(kf), flat_base + (uint32_t)rr.code_of(k));
     }
   }
@@ -1338,6 +1386,8 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
 template <int L, bool G, bool X>
 __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   __shared__ int red[4];
+  __shared__ uint32_t mwords[L == kTrie ? 256 : 1];   // dense row: its child mask, and
+  __shared__ uint32_t mprefix[L == kTrie ? 256 : 1];  // the children before each word
   __shared__ float redf[X ? 4 : 1];
   __shared__ double redd[X ? 4 : 1];
   __shared__ uint32_t hist[G ? 256 : 1];
@@ -1348,13 +1398,13 @@ __global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
   int fl = 0;
   const BeamRow b = beam_setup(a, slot, fl);
   RowRegs<L, G> rr;
-  if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl);
+  if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl, b.mask);
   if constexpr (X) {
     // pilot slots' lse came from the pilot kernel; the others are computed here
     const bool pilot = b.slot - b.rd.boff < (G ? b.rd.n_pilot_s : b.rd.n_pilot);
     if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, !pilot, redf, redd, fl);
   }
-  const int n_out = keep_beam<L, G>(a, b, rr, fl, red, hist, scr, red32);
+  const int n_out = keep_beam<L, G>(a, b, rr, fl, red, hist, scr, red32, mwords, mprefix);
   if (tid == 0) a.surv_count[slot] = n_out;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);

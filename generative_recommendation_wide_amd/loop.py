@@ -15,7 +15,8 @@ import torch
 
 class DecodeLoop:
     def __init__(self, ws, S: int, C: int, trie=None, device="cuda"):
-        """ws: a bound Workspace; trie: (row_ptr, code, n_internal) device tensors or None."""
+        """ws: a bound Workspace; trie: (row_ptr, code, n_internal) device tensors, optionally
+        followed by (dense_slot, dense_mask) for nodes with dense child masks, or None."""
         from . import _lib  # noqa: F401  (the library must be loaded)
         self.ws, self.S, self.C = ws, S, C
         sumW = ws.sumW
@@ -32,9 +33,15 @@ class DecodeLoop:
     def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0,
                     raw_logits: bool = False):
         """Selection at depth d; with noise, the Gumbel top-k at the given temperature; with
-        raw_logits, `logprobs` holds raw logits and the row log-softmax is fused in."""
-        from . import beam_select, beam_select_gumbel, beam_select_logits
+        raw_logits, `logprobs` holds raw logits and the row log-softmax is fused in.  A trie
+        with dense child masks (five-tuple) goes through beam_select_ex."""
+        from . import beam_select, beam_select_ex, beam_select_gumbel, beam_select_logits
         cur, nxt = d % 2, (d + 1) % 2
+        if self.trie is not None and len(self.trie) > 3:
+            beam_select_ex(self.ws, logprobs, self.scores[cur], self.nodes[cur], self.trie, self.W, self.K, self.C,
+                           self.tokens[d], self.parents[d], self.scores[nxt], self.nodes[nxt], noise, temperature,
+                           raw_logits, stream)
+            return
         row_ptr, code, n_int = self.trie if self.trie is not None else (None, None, 0)
         if raw_logits:
             beam_select_logits(self.ws, logprobs, noise, temperature, self.scores[cur], self.nodes[cur],

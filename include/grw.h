@@ -5,6 +5,7 @@
  *   beam_select       trie-masked per-beam top_k, then the global beam_width-of-pool select
  *   beam_select_gumbel the same with Gumbel-perturbed ordering keys (temperature > 0)
  *   beam_select_logits the same from raw logits, with the row log-softmax fused in
+ *   beam_select_ex     every selection option at once, with a dense-or-CSR trie
  *   beam_attn_decode  beam attention over a shared prompt KV plus per-beam decode KV
  *                     reached through parent pointers, in three stages
  *                     (shared stage, unshared stage, online-softmax merge)
@@ -265,6 +266,55 @@ int beam_select_logits(grw_ws* ws, const float* logits, const float* noise, floa
                        int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
                        int32_t* out_token, int32_t* out_parent, float* out_score,
                        int32_t* out_node, void* stream);
+
+/*
+ * The trie of beam_select_ex: the CSR arrays of beam_select, and optionally a dense child
+ * bit mask for some nodes (FlashRec announcement: the fused SID trie is dense or CSR).  The
+ * CSR stays complete; a mask is another view of its node's row that lets the selection read
+ * the node's log-prob row in full lines, which is cheaper than gathering its children when
+ * the node has many.  All pointers are device memory.
+ *   dense_slot  [n_internal] int32: index of the node's mask, or -1 (CSR only); NULL: none
+ *   dense_mask  [n_dense][(C + 31) / 32] uint32: bit c % 32 of word c / 32 is set when code
+ *               c is a child of the node (must agree with the CSR row; a code set here but
+ *               missing from the CSR row raises GRW_FLAG_CHILD_MISSING)
+ */
+typedef struct grw_trie {
+  const int32_t* row_ptr;
+  const int32_t* code;
+  int32_t n_internal;
+  const int32_t* dense_slot;
+  const uint32_t* dense_mask;
+} grw_trie;
+
+/* Options of beam_select_ex. */
+typedef struct grw_select_opts {
+  const float* noise;       /* Gumbel noise [sumW][C] (as for beam_select_gumbel) or NULL */
+  float temperature;        /* with noise: finite, >= 0 */
+  int32_t raw_logits;       /* 1: the input holds raw logits (as for beam_select_logits) */
+} grw_select_opts;
+
+/*
+ * beam_select_ex — the selection step with every option: trie given by a grw_trie (host
+ * struct; NULL for unconstrained selection), and opts (host struct; NULL for the
+ * deterministic selection from log-probabilities).  beam_select, beam_select_gumbel and
+ * beam_select_logits are this call with a CSR-only trie and the corresponding options;
+ * results do not depend on which nodes have dense masks.  Arguments and errors otherwise
+ * as for beam_select.
+ */
+int beam_select_ex(grw_ws* ws, const float* input, const float* beam_scores, const int32_t* beam_node,
+                   const grw_trie* trie, const grw_select_opts* opts, int32_t W, int32_t K, int32_t C,
+                   int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node,
+                   void* stream);
+
+/*
+ * grw_trie_dense_build — host-side: dense child masks for the nodes of a CSR trie with at
+ * least min_fanout children.  All arguments are host memory.  Writes dense_slot[n_internal]
+ * (mask index or -1) and *n_dense; with dense_mask non-NULL also the masks
+ * [n_dense][(C + 31) / 32] (call once with dense_mask NULL to size it).  GRW_EINVAL for
+ * NULL arguments, a decreasing row_ptr or a code outside [0, C).
+ */
+int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_internal, int32_t C,
+                         int32_t min_fanout, int32_t* dense_slot, uint32_t* dense_mask, int32_t* n_dense);
 
 /*
  * grw_backtrack — the semantic-ID tuple of every final beam (xLLM design doc, section

@@ -26,15 +26,22 @@ def make_ws(lib, Ws, Ks, Ps, *, C, S, Hq=16, Hkv=8, D=128, q_dtype="bf16", kv_dt
     return ws
 
 
-def trie_device(trie):
+def trie_device(trie, lib=None, C=None, dense_min_fanout=None):
+    """Device CSR trie tuple; with dense_min_fanout also the dense child masks of the nodes
+    with at least that many children (five-tuple)."""
     if trie is None:
         return None
-    return (torch.from_numpy(trie["row_ptr"]).cuda(), torch.from_numpy(trie["code"]).cuda(),
-            int(trie["n_internal"]))
+    t = (torch.from_numpy(trie["row_ptr"]).cuda(), torch.from_numpy(trie["code"]).cuda(),
+         int(trie["n_internal"]))
+    if dense_min_fanout is None:
+        return t
+    slot, masks = lib.trie_dense_build(trie["row_ptr"], trie["code"], trie["n_internal"], C, dense_min_fanout)
+    masks = masks if masks.size else np.zeros((1, (C + 31) // 32), np.uint32)
+    return t + (torch.from_numpy(slot).cuda(), torch.from_numpy(masks.view(np.int32)).cuda())
 
 
 def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
-                          noise_of_step=None, temperature=0.0, raw_logits=False):
+                          noise_of_step=None, temperature=0.0, raw_logits=False, dense_min_fanout=None):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
     every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
     the steps are the Gumbel-sampled selection at the given temperature; with raw_logits,
@@ -45,7 +52,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
     trie = build_trie_csr(items, C) if items is not None else None
     psets = catalog_prefix_sets(items, C) if items is not None else None
     ws = make_ws(lib, Ws, Ks, [64] * R, C=C, S=S)
-    loop = lib.DecodeLoop(ws, S, C, trie_device(trie))
+    loop = lib.DecodeLoop(ws, S, C, trie_device(trie, lib, C, dense_min_fanout))
     ws.beams_init(loop.scores[0], loop.nodes[0])
     check = list(range(R)) if check is None else list(check)
     state = {r: initial_beams(Ws[r]) for r in check}
