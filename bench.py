@@ -247,6 +247,91 @@ def dense_sweep(seed, dev, reps=10):
     return {"workload": "wide512", "select_loops": rows, "device_flags": flags}
 
 
+def batching_bench(seed, dev, budget=4096, max_requests=128):
+    """The ragged fp8 workload's queue (101 requests: widths 2..100 and one of 1000, top_k =
+    width, prompts 512..8192, 4 steps, one layer, 4-level trie of 2M items) run batch by batch
+    through one workspace, rebound per batch: packed by grw_plan_batches (first fit in queue
+    order under a beam-row slot budget) against one request per batch.  Per batch, the S-step
+    loop (select, then attention) is timed by HIP events; binds are host work outside them.
+    The rate is beam-row steps per second of device time; both packings must give every
+    request the same tokens, parents and scores."""
+    import numpy as np
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    from synth import build_trie_csr, catalog_items, request_shapes, workload
+    wl = workload("mixed_fp8")
+    W, K, P = request_shapes(wl, seed)
+    n, S, C = len(W), wl.S, wl.C
+    Pp = ((P + 63) // 64) * 64
+    g = torch.Generator(device=dev).manual_seed(seed)
+
+    def fp8(*shape):
+        x = torch.randn(*shape, generator=g, device=dev) * 64.0
+        return x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    q = [torch.randn(S, int(w), wl.Hq, wl.D, generator=g, device=dev).to(torch.bfloat16) for w in W]
+    ku = [fp8(S, int(w), wl.Hkv, wl.D) for w in W]
+    vu = [fp8(S, int(w), wl.Hkv, wl.D) for w in W]
+    ks = [fp8(wl.Hkv * int(p) * wl.D) for p in Pp]
+    vs = [fp8(wl.Hkv * int(p) * wl.D) for p in Pp]
+    lps = []
+    for w in W:
+        x = torch.randn(S, int(w), C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
+        lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
+    k_scale = torch.full((wl.Hkv,), 1.0 / 64.0, device=dev)
+    v_scale = torch.full((wl.Hkv,), 1.0 / 64.0, device=dev)
+    t = build_trie_csr(catalog_items(wl, seed), C)
+    trie = (torch.from_numpy(t["row_ptr"]).to(dev), torch.from_numpy(t["code"]).to(dev), t["n_internal"])
+    ws = grw.Workspace(max_requests=max_requests, max_total_beams=budget, max_W=int(W.max()), max_K=int(K.max()),
+                       max_C=C, max_S=S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                       q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
+    rows, results = [], []
+    for name, mr in ((f"first fit, {budget} slots", max_requests), ("one request per batch", 1)):
+        batch_of, nb = grw.plan_batches(W, budget, mr)
+        dev_ms, per_req = 0.0, {}
+        t_wall = time.perf_counter()
+        for b in range(nb):
+            ids = np.flatnonzero(batch_of == b).tolist()
+            ws.bind_batch(W[ids], K[ids], P[ids])
+            qb = torch.cat([q[i] for i in ids], dim=1)
+            kub, vub = torch.cat([ku[i] for i in ids], dim=1), torch.cat([vu[i] for i in ids], dim=1)
+            ksb, vsb = torch.cat([ks[i] for i in ids]), torch.cat([vs[i] for i in ids])
+            lpb = [torch.cat([lps[i][d] for i in ids]) for d in range(S)]
+            out = torch.empty(qb.shape[1], wl.Hq, wl.D, dtype=torch.float32, device=dev)
+            loop = grw.DecodeLoop(ws, S, C, trie, device=dev)
+            layer = dict(q=qb, k_s=ksb, v_s=vsb, k_u=kub, v_u=vub, k_scale=k_scale, v_scale=v_scale)
+            ms = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                loop.run(lpb, [layer], out)
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            dev_ms += min(ms[1:])
+            tok, par = loop.tokens.cpu(), loop.parents.cpu()
+            sc = loop.final_scores().view(torch.int32).cpu()
+            off = 0
+            for i in ids:
+                w = int(W[i])
+                per_req[i] = (tok[:, off:off + w].clone(), par[:, off:off + w].clone(), sc[off:off + w].clone())
+                off += w
+            del qb, kub, vub, ksb, vsb, lpb, out, loop
+        wall = time.perf_counter() - t_wall
+        rows.append({"policy": name, "batches": int(nb), "device_ms": round(dev_ms, 3),
+                     "wall_ms_incl_binds": round(wall * 1e3, 1),
+                     "beam_row_steps_per_s": round(float(W.sum()) * S / (dev_ms / 1e3), 1)})
+        results.append(per_req)
+    same = all(all(torch.equal(a, b) for a, b in zip(results[0][i], results[1][i])) for i in range(n))
+    flags = ws.error_flags()
+    ws.close()
+    return {"workload": "mixed_fp8 queue", "requests": n, "sum_W": int(W.sum()), "slot_budget": budget,
+            "max_requests": max_requests, "policies": rows,
+            "speedup_packed_vs_one_per_batch": round(rows[1]["device_ms"] / rows[0]["device_ms"], 2),
+            "same_results_both_packings": bool(same), "device_flags": flags}
+
+
 def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
     """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
     262144-entry pools): device time of one call with every beam live (the third decode step,
@@ -527,6 +612,8 @@ def main():
                     help="with --select-only: time beam_select_logits on raw logits")
     ap.add_argument("--dense-sweep", action="store_true",
                     help="time the wide512 select loop with dense child masks at several fan-out thresholds")
+    ap.add_argument("--batching", action="store_true",
+                    help="run the ragged fp8 queue packed under a slot budget and one request per batch")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -553,6 +640,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.dense_sweep:
         print(json.dumps(dense_sweep(args.seed, dev)), flush=True)
+        return 0
+    if args.batching:
+        print(json.dumps(batching_bench(args.seed, dev)), flush=True)
         return 0
     if args.select_only:
         print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature,

@@ -195,6 +195,19 @@ def trie_dense_build(row_ptr, code, n_internal: int, C: int, min_fanout: int):
     return slot, masks
 
 
+def plan_batches(W, slot_budget: int, max_requests: int):
+    """Host-side slot-budget batching (see grw_plan_batches): beam widths in queue order ->
+    (batch_of int32 [n], n_batches), first fit in queue order."""
+    import numpy as np
+    W = np.ascontiguousarray(W, dtype=np.int32)
+    batch_of = np.empty(W.size, np.int32)
+    nb = ctypes.c_int32(0)
+    _lib.check("grw_plan_batches", _L.grw_plan_batches(
+        int(W.size), W.ctypes.data if W.size else None, int(slot_budget), int(max_requests),
+        batch_of.ctypes.data if W.size else None, ctypes.byref(nb)))
+    return batch_of, nb.value
+
+
 def grw_backtrack(ws: Workspace, tokens, parents, S: int, sid_out, stream=None):
     """Semantic-ID tuples [sumW][S] of the final beams (see include/grw.h)."""
     _lib.check("grw_backtrack", _L.grw_backtrack(

@@ -21,7 +21,8 @@ STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
             "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "beam_select_gumbel",
-            "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_backtrack", "grw_ws_error",
+            "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_plan_batches", "grw_backtrack",
+            "grw_ws_error",
             "grw_ws_splits", "grw_ws_pool_size", "grw_status_str"]
 
 
@@ -74,6 +75,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "beam_select_ex": [vp, fp, fp, i32p, ctypes.POINTER(GrwTrie), ctypes.POINTER(GrwSelectOpts), i32, i32, i32,
                            i32p, i32p, fp, i32p, vp],
         "grw_trie_dense_build": [vp, vp, i32, i32, i32, vp, vp, ctypes.POINTER(i32)],
+        "grw_plan_batches": [i32, vp, i32, i32, vp, ctypes.POINTER(i32)],
         "grw_backtrack": [vp, i32p, i32p, i32, i32p, vp],
         "grw_ws_error": [vp, vp, ctypes.POINTER(i32)],
         "grw_ws_splits": [vp, i32, ctypes.POINTER(i32)],

@@ -581,6 +581,36 @@ int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_
   return GRW_OK;
 }
 
+int grw_plan_batches(int32_t n, const int32_t* W, int32_t slot_budget, int32_t max_requests,
+                     int32_t* batch_of, int32_t* n_batches) {
+  if (n < 0 || !n_batches || slot_budget < 1 || max_requests < 1) return GRW_EINVAL;
+  if (n > 0 && (!W || !batch_of)) return GRW_EINVAL;
+  for (int32_t i = 0; i < n; ++i)
+    if (W[i] < 1 || W[i] > slot_budget) return GRW_EINVAL;
+  *n_batches = 0;
+  if (n == 0) return GRW_OK;
+  // Max tree over batches 0..n-1 (at most n open): a leaf holds the batch's free rows, or -1
+  // once it holds max_requests requests.  Unopened batches hold the whole budget, so the
+  // leftmost leaf with room for a request is an open batch or the next one to open.
+  int32_t size = 1;
+  while (size < n) size <<= 1;
+  std::vector<int32_t> tree(2 * (size_t)size, slot_budget), count(n, 0);
+  int32_t opened = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t w = W[i];
+    int32_t v = 1;
+    while (v < size) v = tree[2 * v] >= w ? 2 * v : 2 * v + 1;
+    const int32_t b = v - size;    // b <= opened <= i < n: batch `opened` is still empty
+    batch_of[i] = b;
+    opened = std::max(opened, b + 1);
+    const int32_t rows = tree[v] - w;
+    tree[v] = ++count[b] >= max_requests ? -1 : rows;
+    for (v >>= 1; v >= 1; v >>= 1) tree[v] = std::max(tree[2 * v], tree[2 * v + 1]);
+  }
+  *n_batches = opened;
+  return GRW_OK;
+}
+
 int beam_select_logits(grw_ws* w, const float* logits, const float* noise, float temperature,
                        const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
                        const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K,

@@ -317,6 +317,26 @@ int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_
                          int32_t min_fanout, int32_t* dense_slot, uint32_t* dense_mask, int32_t* n_dense);
 
 /*
+ * grw_plan_batches — host-side slot-budget batching (FlashRec announcement: scheduling by a
+ * beam-row slot budget, so that the rows of several requests share one step; FlashRec
+ * deployment guide, wide-beam section: the slot count bounds how many wide requests run
+ * together).  Packs a queue of n requests with beam widths W[0..n) into batches whose total
+ * beam rows stay within slot_budget and which hold at most max_requests requests each.
+ * Policy: first fit in queue order — request i joins the lowest-numbered batch that still
+ * has room for it (rows and request count), else opens the next batch; batches are numbered
+ * in the order they open and keep their requests in queue order.  Each batch is one
+ * grw_ws_bind_batch of a workspace created with max_total_beams >= slot_budget and
+ * max_requests >= max_requests.
+ *   W         [n] int32 host, each in [1, slot_budget]
+ *   batch_of  [n] int32 host, written: batch index of each request
+ *   n_batches int32 host, written: the number of batches (0 for n == 0)
+ * GRW_EINVAL for n < 0, NULL pointers (W and batch_of may be NULL when n == 0),
+ * slot_budget < 1, max_requests < 1, or a width outside [1, slot_budget].  O(n log n).
+ */
+int grw_plan_batches(int32_t n, const int32_t* W, int32_t slot_budget, int32_t max_requests,
+                     int32_t* batch_of, int32_t* n_batches);
+
+/*
  * grw_backtrack — the semantic-ID tuple of every final beam (xLLM design doc, section
  * 4.1.1: the item id is the fixed-length sequence of generated tokens).
  *   tokens, parents  [S][sumW] int32, the out_token / out_parent of steps 0..S-1

@@ -13,7 +13,9 @@ What it computes is the plain definition of the step, not the method's fast rout
 * selection: per-beam full stable sort of the trie-valid candidates keeping top_k, then a
   full sort of the beam_width x top_k pool keeping beam_width (same doc, §4.1.1 "model
   input/output characteristics"; FlashRec announcement: illegal semantic IDs are never
-  candidates).  Validity is decided from the raw catalog item list, never from a CSR.
+  candidates).  Validity is decided from the raw catalog item list, never from a CSR;
+* slot-budget batching: first fit in queue order of requests into batches of at most a
+  given number of beam rows (FlashRec announcement: scheduling by beam-row slot budget).
 
 Pins (tests/test_oracle_*.py) tie every function to something other than itself:
 exhaustive pure-Python enumeration, closed forms, special cases equal to library
@@ -22,3 +24,4 @@ routines, and invariants.  No function here is "parity unpinned".
 from .numformats import decode_bf16_bits, decode_e4m3fn_bits, decode_stored  # noqa: F401
 from .attention import attend_concat, oracle_attention  # noqa: F401
 from .select import catalog_prefix_sets, oracle_select, oracle_beam_search  # noqa: F401
+from .batching import oracle_plan_batches  # noqa: F401
