@@ -247,6 +247,49 @@ def dense_sweep(seed, dev, reps=10):
     return {"workload": "wide512", "select_loops": rows, "device_flags": flags}
 
 
+def overlap_timings(wl, st, steps):
+    """The two-stream attention (unshared stage on a side stream beside the shared stage,
+    merge after both) against the default path (shared stage, then the unshared stage with
+    the merge fused in): per-layer attention at the last depth (HIP graph of every layer,
+    4 times, best of 5 replays) and the whole decode loop as a replayed graph."""
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    ws, loop, layers, out, lps = st["ws"], st["loop"], st["layers"], st["out"], st["lps"]
+    loop2 = grw.DecodeLoop(ws, wl.S, wl.C, st["trie"], device=out.device, overlap=True)
+    loop2.run(lps, layers, out)
+    torch.cuda.synchronize()
+    d = wl.S - 1
+    res = {}
+    for name, lp in (("fused", loop), ("overlap", loop2)):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(4):
+                for L in layers:
+                    lp.attn_step(d, L, out)
+        graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / (4 * len(layers)))
+        res[f"{name}_attention_us_per_layer"] = round(min(ts), 2)
+        del graph
+    graph = loop2.capture(lps, layers, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    res["overlap_graph_replay_value"] = round(wl.S * steps / (time.perf_counter() - t0), 2)
+    del graph, loop2
+    return res
+
+
 def batching_bench(seed, dev, budget=4096, max_requests=128):
     """The ragged fp8 workload's queue (101 requests: widths 2..100 and one of 1000, top_k =
     width, prompts 512..8192, 4 steps, one layer, 4-level trie of 2M items) run batch by batch
@@ -683,6 +726,8 @@ def main():
     graph_value = decode_steps / graph_wall
     log(f"[bench] graph replay of {args.steps} steps: wall {graph_wall * 1e3:.2f} ms")
 
+    overlap = overlap_timings(wl, st, args.steps)
+    log(f"[bench] two-stream attention: {overlap}")
     if args.stage_reps > 0:
         stages = stage_timings(wl, st, args.stage_reps)
     else:
@@ -739,6 +784,7 @@ def main():
                    "trie": None if wl.catalog is None else f"{wl.catalog[0]} {wl.catalog[1]} items",
                    "device_flags": flags},
         "graph_replay_value": round(graph_value, 2),
+        "two_stream_attention": overlap,
         "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
         "select_roofline": sel_roof,

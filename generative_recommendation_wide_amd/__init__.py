@@ -122,6 +122,20 @@ def beam_attn_decode_stages(ws: Workspace, q, k_shared, v_shared, k_scale, v_sca
         _stream(stream)))
 
 
+def beam_attn_decode_overlap(ws: Workspace, q, k_shared, v_shared, k_scale, v_scale, k_unshared,
+                             v_unshared, parent_idx, step: int, out, side_stream, stream=None):
+    """beam_attn_decode with the unshared stage on side_stream (a torch.cuda.Stream other
+    than ``stream``), overlapping the shared stage; the merge runs on ``stream``."""
+    if side_stream is None:
+        raise ValueError("beam_attn_decode_overlap needs a side stream")
+    _lib.check("beam_attn_decode_overlap", _L.beam_attn_decode_overlap(
+        ws.handle, _ptr(q, (torch.float32, torch.bfloat16), "q"), _ptr(k_shared, _ANY_KV, "k_shared"),
+        _ptr(v_shared, _ANY_KV, "v_shared"), _ptr(k_scale, _F32, "k_scale"), _ptr(v_scale, _F32, "v_scale"),
+        _ptr(k_unshared, _ANY_KV, "k_unshared"), _ptr(v_unshared, _ANY_KV, "v_unshared"),
+        _ptr(parent_idx, _I32, "parent_idx"), int(step), _ptr(out, _F32, "out"), _stream(stream),
+        side_stream.cuda_stream))
+
+
 def beam_select(ws: Workspace, logprobs, beam_scores, beam_node, trie_row_ptr, trie_code,
                 trie_n_internal: int, W: int, K: int, C: int, out_token, out_parent, out_score,
                 out_node, stream=None):

@@ -20,7 +20,7 @@ FLAG_BAD_NOISE = 64
 STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
-            "beam_attn_decode", "beam_attn_decode_stages", "beam_select", "beam_select_gumbel",
+            "beam_attn_decode", "beam_attn_decode_stages", "beam_attn_decode_overlap", "beam_select", "beam_select_gumbel",
             "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_plan_batches", "grw_backtrack",
             "grw_ws_error",
             "grw_ws_splits", "grw_ws_pool_size", "grw_status_str"]
@@ -67,6 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "grw_beams_init": [vp, fp, i32p, vp],
         "beam_attn_decode": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, vp],
         "beam_attn_decode_stages": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, i32, vp],
+        "beam_attn_decode_overlap": [vp, vp, vp, vp, fp, fp, vp, vp, i32p, i32, fp, vp, vp],
         "beam_select": [vp, fp, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp, i32p, vp],
         "beam_select_gumbel": [vp, fp, fp, ctypes.c_float, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp,
                                i32p, vp],

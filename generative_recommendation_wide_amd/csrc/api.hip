@@ -40,6 +40,8 @@ struct grw_ws {
   uint64_t* d_pilot_buf = nullptr;
   uint32_t* d_step_state = nullptr;    // [max_requests]: pilots finished in the current step
   int32_t* d_flags = nullptr;
+  // fork and join events of the two-stream attention
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // pinned host staging for the bind upload
   void* h_stage = nullptr;
   size_t stage_bytes = 0;
@@ -96,6 +98,8 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_pilot_buf);
   (void)hipFree(w->d_flags);
   if (w->h_stage) (void)hipHostFree(w->h_stage);
+  if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
+  if (w->ev_join) (void)hipEventDestroy(w->ev_join);
 }
 
 // Shared-stage work lists of the MFMA kernels.  Requests with bf16 KV and more than 128
@@ -281,6 +285,9 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
       st = GRW_ENOMEM;
     }
   }
+  if (st == GRW_OK && (hipEventCreateWithFlags(&w->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                       hipEventCreateWithFlags(&w->ev_join, hipEventDisableTiming) != hipSuccess))
+    st = GRW_EDEVICE;
   if (st == GRW_OK) {
     if (hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
         hipMemset(w->d_step_state, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
@@ -410,12 +417,13 @@ int beam_attn_decode(grw_ws* w, const void* q, const void* k_shared, const void*
                                  parent_idx, step, out, 7, stream);
 }
 
-int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, const void* v_shared,
-                            const float* k_scale, const float* v_scale, const void* k_unshared,
-                            const void* v_unshared, const int32_t* parent_idx, int32_t step,
-                            float* out, int32_t stages, void* stream) {
+namespace {
+
+// Validates the attention call and fills its kernel arguments.
+int attn_args(grw_ws* w, const void* q, const void* k_shared, const void* v_shared, const float* k_scale,
+              const float* v_scale, const void* k_unshared, const void* v_unshared,
+              const int32_t* parent_idx, int32_t step, float* out, AttnArgs& a) {
   if (!w) return GRW_EINVAL;
-  if (stages < 1 || stages > 7) return GRW_EINVAL;
   if (!w->bound) return GRW_ESTATE;
   const grw_limits& L = w->lim;
   if (!q || !k_shared || !v_shared || !k_unshared || !v_unshared || !parent_idx || !out)
@@ -423,7 +431,7 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
   const bool fp8 = L.kv_dtype == GRW_FP8_E4M3;
   if (fp8 != (k_scale != nullptr) || fp8 != (v_scale != nullptr)) return GRW_EINVAL;
   if (step < 0 || step >= L.max_S) return GRW_EINVAL;
-  AttnArgs a{};
+  a = AttnArgs{};
   a.req = w->d_req;
   a.slot_req = w->d_slot_req;
   a.q = q;
@@ -448,16 +456,30 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
   a.g = L.Hq / L.Hkv;
   a.q_dtype = L.q_dtype;
   a.kv_dtype = L.kv_dtype;
+  return GRW_OK;
+}
+
+hipError_t launch_shared_stage(grw_ws* w, const AttnArgs& a, hipStream_t s) {
+  if (!w->mfma) return launch_attn_shared_valu(a, w->d_work, w->n_work, s);
+  hipError_t e = launch_attn_shared_lds(a, w->d_work, w->n_wide, s);
+  if (e == hipSuccess) e = launch_attn_shared_mfma(a, w->d_work + w->n_wide, w->n_work - w->n_wide, s);
+  return e;
+}
+
+}  // namespace
+
+int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, const void* v_shared,
+                            const float* k_scale, const float* v_scale, const void* k_unshared,
+                            const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                            float* out, int32_t stages, void* stream) {
+  if (stages < 1 || stages > 7) return GRW_EINVAL;
+  AttnArgs a;
+  const int st = attn_args(w, q, k_shared, v_shared, k_scale, v_scale, k_unshared, v_unshared, parent_idx,
+                           step, out, a);
+  if (st != GRW_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
-  if (stages & GRW_STAGE_SHARED) {
-    if (w->mfma) {
-      e = launch_attn_shared_lds(a, w->d_work, w->n_wide, s);
-      if (e == hipSuccess) e = launch_attn_shared_mfma(a, w->d_work + w->n_wide, w->n_work - w->n_wide, s);
-    } else {
-      e = launch_attn_shared_valu(a, w->d_work, w->n_work, s);
-    }
-  }
+  if (stages & GRW_STAGE_SHARED) e = launch_shared_stage(w, a, s);
   const int um = stages & (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE);
   if (e == hipSuccess && um == (GRW_STAGE_UNSHARED | GRW_STAGE_MERGE)) {
     e = launch_attn_unshared_merge(a, s);        // merge fused into the unshared epilogue
@@ -465,6 +487,28 @@ int beam_attn_decode_stages(grw_ws* w, const void* q, const void* k_shared, cons
     if (e == hipSuccess && (stages & GRW_STAGE_UNSHARED)) e = launch_attn_unshared(a, s);
     if (e == hipSuccess && (stages & GRW_STAGE_MERGE)) e = launch_attn_merge(a, s);
   }
+  return hip_status(e);
+}
+
+int beam_attn_decode_overlap(grw_ws* w, const void* q, const void* k_shared, const void* v_shared,
+                             const float* k_scale, const float* v_scale, const void* k_unshared,
+                             const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                             float* out, void* stream, void* side_stream) {
+  if (!side_stream || side_stream == stream) return GRW_EINVAL;
+  AttnArgs a;
+  const int st = attn_args(w, q, k_shared, v_shared, k_scale, v_scale, k_unshared, v_unshared, parent_idx,
+                           step, out, a);
+  if (st != GRW_OK) return st;
+  hipStream_t s = (hipStream_t)stream, side = (hipStream_t)side_stream;
+  // fork: the unshared stage waits for what `stream` already holds (the parent pointers)
+  hipError_t e = hipEventRecord(w->ev_fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, w->ev_fork, 0);
+  if (e == hipSuccess) e = launch_attn_unshared(a, side);
+  if (e == hipSuccess) e = hipEventRecord(w->ev_join, side);
+  if (e == hipSuccess) e = launch_shared_stage(w, a, s);
+  // join: the merge needs both partials
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, w->ev_join, 0);
+  if (e == hipSuccess) e = launch_attn_merge(a, s);
   return hip_status(e);
 }
 

@@ -14,9 +14,11 @@ import torch
 
 
 class DecodeLoop:
-    def __init__(self, ws, S: int, C: int, trie=None, device="cuda"):
+    def __init__(self, ws, S: int, C: int, trie=None, device="cuda", overlap: bool = False):
         """ws: a bound Workspace; trie: (row_ptr, code, n_internal) device tensors, optionally
-        followed by (dense_slot, dense_mask) for nodes with dense child masks, or None."""
+        followed by (dense_slot, dense_mask) for nodes with dense child masks, or None;
+        overlap: run each layer's unshared stage on a side stream beside its shared stage
+        (beam_attn_decode_overlap) instead of the fused unshared + merge kernel."""
         from . import _lib  # noqa: F401  (the library must be loaded)
         self.ws, self.S, self.C = ws, S, C
         sumW = ws.sumW
@@ -29,6 +31,7 @@ class DecodeLoop:
         self.tokens = torch.empty(S, sumW, dtype=torch.int32, device=dev)
         self.parents = torch.empty(S, sumW, dtype=torch.int32, device=dev)   # parent_idx
         self.sid = torch.empty(sumW, S, dtype=torch.int32, device=dev)
+        self.side_stream = torch.cuda.Stream(device=dev) if overlap else None
 
     def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0,
                     raw_logits: bool = False):
@@ -57,9 +60,13 @@ class DecodeLoop:
                                self.scores[nxt], self.nodes[nxt], stream)
 
     def attn_step(self, d: int, layer, out, stream=None):
-        from . import beam_attn_decode
-        beam_attn_decode(self.ws, layer["q"][d], layer["k_s"], layer["v_s"], layer.get("k_scale"),
-                         layer.get("v_scale"), layer["k_u"], layer["v_u"], self.parents, d, out, stream)
+        from . import beam_attn_decode, beam_attn_decode_overlap
+        args = (self.ws, layer["q"][d], layer["k_s"], layer["v_s"], layer.get("k_scale"), layer.get("v_scale"),
+                layer["k_u"], layer["v_u"], self.parents, d, out)
+        if self.side_stream is not None:
+            beam_attn_decode_overlap(*args, self.side_stream, stream)
+        else:
+            beam_attn_decode(*args, stream)
 
     def run(self, logprobs, layers, out, stream=None, steps=None, noise=None, temperature: float = 0.0,
             raw_logits: bool = False):

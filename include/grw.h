@@ -177,6 +177,26 @@ int beam_attn_decode_stages(grw_ws* ws, const void* q, const void* k_shared,
                             int32_t stages, void* stream);
 
 /*
+ * beam_attn_decode_overlap — beam_attn_decode with the shared and unshared stages on two
+ * streams (xLLM design doc, section 4.2.2: shared, unshared and merge placed on different
+ * execution units and queues as a pipeline, the two stages overlapping, with as few
+ * synchronisation points as possible).  The unshared stage runs on side_stream once the work
+ * enqueued on `stream` before this call is done (one event), writing its partial into the
+ * workspace; the shared stage runs on `stream`; the merge runs on `stream` after both (a
+ * second event).  Work enqueued on `stream` afterwards sees `out` complete; side_stream needs
+ * no synchronisation by the caller.  The two events belong to the workspace, so calls on one
+ * workspace must not overlap each other.  The result equals beam_attn_decode_stages with
+ * GRW_STAGE_SHARED, then GRW_STAGE_UNSHARED, then GRW_STAGE_MERGE, bit for bit.  Graph
+ * capture of `stream` takes side_stream into the capture through the first event.
+ * side_stream must differ from stream (GRW_EINVAL otherwise, and for a NULL side_stream);
+ * other arguments and errors as for beam_attn_decode.
+ */
+int beam_attn_decode_overlap(grw_ws* ws, const void* q, const void* k_shared, const void* v_shared,
+                             const float* k_scale, const float* v_scale, const void* k_unshared,
+                             const void* v_unshared, const int32_t* parent_idx, int32_t step,
+                             float* out, void* stream, void* side_stream);
+
+/*
  * beam_select — one selection step for every request of the bound batch (xLLM design doc,
  * sections 4.1.1 and 4.3; FlashRec's trie-constrained expansion).
  *

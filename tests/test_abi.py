@@ -71,6 +71,8 @@ def test_null_handles_rejected(clib):
     assert clib.grw_ws_destroy(None) == 1
     assert clib.grw_ws_bind_batch(None, 1, None, None, None, None) == 1
     assert clib.beam_attn_decode(None, None, None, None, None, None, None, None, None, 0, None, None) == 1
+    assert clib.beam_attn_decode_overlap(None, None, None, None, None, None, None, None, None, 0, None, None,
+                                         None) == 1
     assert clib.beam_select(None, *([None] * 5), 0, 1, 1, 1, None, None, None, None, None) == 1
     f = clib.beam_select_gumbel
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] * 4 + \
