@@ -290,6 +290,64 @@ def overlap_timings(wl, st, steps):
     return res
 
 
+def fanout_bench(seed, dev, steps=3, reps=10):
+    """First-step fan-out on the ultra-wide shape (W = 5000, top_k = 64, 151936-token rows,
+    no trie): the first step expanding the prompt beam to its best 5000 children against
+    the plain first step (top_k = 64).  Device time of the first step and of the first
+    `steps` steps (HIP graphs, best of 5 replays of `reps` loops), and the live beams after
+    each step."""
+    import torch
+
+    import generative_recommendation_wide_amd as grw
+    from synth import request_shapes, workload
+    wl = workload("ultra5000")
+    W, K, P = request_shapes(wl, seed)
+    sumW, C = int(W.sum()), wl.C
+    g = torch.Generator(device=dev).manual_seed(seed)
+    lps = []
+    for _ in range(steps):
+        x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float32) * wl.logit_sigma
+        lps.append(torch.log_softmax(x.double(), dim=-1).to(torch.float32).clamp_max_(0.0))
+        del x
+    ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
+                       max_C=C, max_S=wl.S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                       q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
+    ws.bind_batch(W, K, P)
+    rows = []
+    for fan in (False, True):
+        loop = grw.DecodeLoop(ws, wl.S, C, None, device=dev, fanout=fan)
+        res = {"first_step": "fan-out to W" if fan else "top_k"}
+        for n in (1, steps):
+            def run(n=n):
+                ws.beams_init(loop.scores[0], loop.nodes[0])
+                for d in range(n):
+                    loop.select_step(d, lps[d])
+            run()
+            torch.cuda.synchronize()
+            if n == steps:
+                res["live_beams_after_each_step"] = [int((loop.parents[d] >= 0).sum().item()) for d in range(steps)]
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    run()
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+            res[f"us_first_{n}_steps"] = round(min(ts), 1)
+            del graph
+        rows.append(res)
+        del loop
+    flags = ws.error_flags()
+    ws.close()
+    return {"workload": "ultra5000 (select only)", "beam_width": int(W.max()), "top_k": int(K.max()),
+            "codes": C, "variants": rows, "device_flags": flags}
+
+
 def batching_bench(seed, dev, budget=4096, max_requests=128):
     """The ragged fp8 workload's queue (101 requests: widths 2..100 and one of 1000, top_k =
     width, prompts 512..8192, 4 steps, one layer, 4-level trie of 2M items) run batch by batch
@@ -657,6 +715,8 @@ def main():
                     help="time the wide512 select loop with dense child masks at several fan-out thresholds")
     ap.add_argument("--batching", action="store_true",
                     help="run the ragged fp8 queue packed under a slot budget and one request per batch")
+    ap.add_argument("--fanout", action="store_true",
+                    help="time the first-step fan-out against the plain first step on the ultra-wide shape")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summary-out", default=None)
@@ -683,6 +743,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.dense_sweep:
         print(json.dumps(dense_sweep(args.seed, dev)), flush=True)
+        return 0
+    if args.fanout:
+        print(json.dumps(fanout_bench(args.seed, dev)), flush=True)
         return 0
     if args.batching:
         print(json.dumps(batching_bench(args.seed, dev)), flush=True)

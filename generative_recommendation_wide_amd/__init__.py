@@ -175,17 +175,17 @@ def beam_select_logits(ws: Workspace, logits, noise, temperature: float, beam_sc
 
 def beam_select_ex(ws: Workspace, input, beam_scores, beam_node, trie, W: int, K: int, C: int, out_token,
                    out_parent, out_score, out_node, noise=None, temperature: float = 0.0, raw_logits: bool = False,
-                   stream=None):
+                   stream=None, fanout: bool = False):
     """The selection step with every option (see include/grw.h).  trie: None, or a tuple
     (row_ptr, code, n_internal) or (row_ptr, code, n_internal, dense_slot, dense_mask) of
-    device tensors (n_internal an int)."""
+    device tensors (n_internal an int); fanout: the first-step fan-out."""
     t = None
     if trie is not None:
         row_ptr, code, n_int = trie[:3]
         dslot, dmask = (trie[3], trie[4]) if len(trie) > 3 else (None, None)
         t = _lib.GrwTrie(_ptr(row_ptr, _I32, "row_ptr"), _ptr(code, _I32, "code"), int(n_int),
                          _ptr(dslot, _I32, "dense_slot"), _ptr(dmask, (torch.int32, torch.uint32), "dense_mask"))
-    o = _lib.GrwSelectOpts(_ptr(noise, _F32, "noise"), float(temperature), int(bool(raw_logits)))
+    o = _lib.GrwSelectOpts(_ptr(noise, _F32, "noise"), float(temperature), int(bool(raw_logits)), int(bool(fanout)))
     _lib.check("beam_select_ex", _L.beam_select_ex(
         ws.handle, _ptr(input, _F32, "input"), _ptr(beam_scores, _F32, "beam_scores"),
         _ptr(beam_node, _I32, "beam_node"), ctypes.byref(t) if t is not None else None, ctypes.byref(o),

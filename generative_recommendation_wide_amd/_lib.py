@@ -38,7 +38,8 @@ class GrwTrie(ctypes.Structure):
 
 
 class GrwSelectOpts(ctypes.Structure):
-    _fields_ = [("noise", ctypes.c_void_p), ("temperature", ctypes.c_float), ("raw_logits", ctypes.c_int32)]
+    _fields_ = [("noise", ctypes.c_void_p), ("temperature", ctypes.c_float), ("raw_logits", ctypes.c_int32),
+                ("first_step_fanout", ctypes.c_int32)]
 
 
 class GrwError(RuntimeError):

@@ -519,7 +519,7 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
                 const float* beam_scores, const int32_t* beam_node, const int32_t* trie_row_ptr,
                 const int32_t* trie_code, int32_t trie_n_internal, int32_t W, int32_t K, int32_t C,
                 int32_t* out_token, int32_t* out_parent, float* out_score, int32_t* out_node, void* stream,
-                const int32_t* dense_slot = nullptr, const uint32_t* dense_mask = nullptr) {
+                const int32_t* dense_slot = nullptr, const uint32_t* dense_mask = nullptr, bool fanout = false) {
   if (!w) return GRW_EINVAL;
   if (!w->bound) return GRW_ESTATE;
   const grw_limits& L = w->lim;
@@ -533,6 +533,10 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   if ((const void*)out_score == (const void*)beam_scores || (const void*)out_node == (const void*)beam_node)
     return GRW_EINVAL;
   if ((dense_slot != nullptr) != (dense_mask != nullptr) || (dense_slot && !trie)) return GRW_EINVAL;
+  // a fan-out wider than kMaxK keeps the prompt beam's whole row in the request's pool region
+  if (fanout && w->maxW > kMaxK)
+    for (int r = 0; r < w->R; ++r)
+      if (w->req[r].W > kMaxK && (int64_t)C > (int64_t)w->req[r].W * w->req[r].K) return GRW_EUNSUPPORTED;
   SelArgs a{};
   a.req = w->d_req;
   a.slot_req = w->d_slot_req;
@@ -549,6 +553,7 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   a.dense_slot = trie ? dense_slot : nullptr;
   a.dense_mask = trie ? dense_mask : nullptr;
   a.mask_words = (C + 31) / 32;
+  a.fanout = fanout ? 1 : 0;
   a.C = C;
   a.sumW = w->sumW;
   a.R = w->R;
@@ -592,11 +597,13 @@ int beam_select_ex(grw_ws* w, const float* input, const float* beam_scores, cons
   const float* noise = opts ? opts->noise : nullptr;
   const float temperature = opts ? opts->temperature : 0.0f;
   if (opts && opts->raw_logits != 0 && opts->raw_logits != 1) return GRW_EINVAL;
+  if (opts && opts->first_step_fanout != 0 && opts->first_step_fanout != 1) return GRW_EINVAL;
   if (noise && (!(temperature >= 0.0f) || !std::isfinite(temperature))) return GRW_EINVAL;
   return select_step(w, input, opts && opts->raw_logits, noise, temperature, beam_scores, beam_node,
                      trie ? trie->row_ptr : nullptr, trie ? trie->code : nullptr, trie ? trie->n_internal : 0,
                      W, K, C, out_token, out_parent, out_score, out_node, stream,
-                     trie ? trie->dense_slot : nullptr, trie ? trie->dense_mask : nullptr);
+                     trie ? trie->dense_slot : nullptr, trie ? trie->dense_mask : nullptr,
+                     opts && opts->first_step_fanout);
 }
 
 int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_internal, int32_t C,

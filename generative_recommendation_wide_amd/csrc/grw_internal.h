@@ -87,6 +87,8 @@ struct SelArgs {
   const int32_t* dense_slot;    // [n_internal] mask index of each node or -1; NULL: CSR only
   const uint32_t* dense_mask;   // [n_dense][mask_words] child bit masks
   int32_t mask_words;           // (C + 31) / 32
+  int32_t fanout;               // 1: first-step fan-out (only each request's first slot expands,
+                                //    keeping its top W_r candidates instead of top_k)
   int32_t C;
   int32_t sumW, R;
   uint64_t* pool;           // per request: W_r regions of K_r entries (one per beam slot)

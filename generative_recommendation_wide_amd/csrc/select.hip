@@ -585,6 +585,18 @@ __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
 // wait until this thread's stores are acknowledged at device scope
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Candidates a beam keeps: top_k, or at a first-step fan-out the request's beam width.  A
+// fan-out wider than the per-beam selection holds (kMaxK) keeps every candidate instead,
+// up to the request's whole pool region (W_r * K_r entries, at least the row length), and
+// leaves the cut to W_r to the W-of-pool stage.
+__device__ __forceinline__ int keep_k(const SelArgs& a, const ReqDesc& rd) {
+  return !a.fanout ? rd.K : (rd.W <= kMaxK ? rd.W : rd.W * rd.K);
+}
+// Whether a slot expands: every slot, or at a first-step fan-out only the request's first.
+__device__ __forceinline__ bool expands(const SelArgs& a, int slot, const ReqDesc& rd) {
+  return !a.fanout || slot == rd.boff;
+}
+
 // --------------------------------------------------------------------------------------
 // pilots and the request bound
 // --------------------------------------------------------------------------------------
@@ -615,7 +627,7 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   const int32_t* codes = nullptr;
   uint64_t best = 0;
   const uint32_t* mask = nullptr;
-  if (s != -INFINITY && !__builtin_isnan(s) && beam_row(a, slot, cnt, codes, &mask)) {
+  if (s != -INFINITY && !__builtin_isnan(s) && expands(a, slot, rd) && beam_row(a, slot, cnt, codes, &mask)) {
     if (cnt <= kOnePass) {
       const int lay = row_layout(a, codes, lprow);
       if (lay == kFull) best = row_best<kFull, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
@@ -697,7 +709,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
   uint32_t tau = a.bound[r];
   // a beam below the bound keeps nothing: no key exceeds its beam's score (noise can lift
   // an ordering key above the score, so the sampled selection reads every live beam)
-  bool live = s != -INFINITY && !__builtin_isnan(s) && (G || ordered_key(s) >= tau);
+  bool live = s != -INFINITY && !__builtin_isnan(s) && expands(a, slot, rd) && (G || ordered_key(s) >= tau);
   if (__builtin_isnan(s)) fl |= GRW_FLAG_NAN_LOGPROB;
   if (live && !beam_row(a, slot, cnt, codes)) {
     fl |= GRW_FLAG_BAD_NODE;
@@ -706,8 +718,8 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
   const float* lprow = a.logprobs + (size_t)slot * a.C;
   const float* grow = G ? a.noise + (size_t)slot * a.C : nullptr;
   const uint32_t flat_base = (uint32_t)j * (uint32_t)a.C;
-  uint64_t* region = a.pool + rd.pool_off + (size_t)j * rd.K;
-  const int K = rd.K;
+  const int K = keep_k(a, rd);
+  uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
   int n_out = 0;
 
   if (live && cnt <= kOnePass) {
@@ -765,6 +777,33 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
         if (v[k] != 0 && v[k] >= T) region[p++] = v[k];
       n_out = min(total, K);                     // the entries written (n_out by construction)
     }
+  } else if (live && K >= cnt) {
+    // ---- long row whose every candidate fits the region (a wide fan-out): no top-K, the
+    // candidates at or above the bound go straight to the region ----
+    if (tid == 0) cnt_s = 0;
+    __syncthreads();
+    for (int base = 0; base < cnt; base += 1024) {
+      uint64_t e[4];
+      int ne = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = base + tid + 256 * k;
+        if (i < cnt) {
+          const int c = codes ? codes[i] : i;
+          if ((unsigned)c >= (unsigned)a.C) {
+            fl |= GRW_FLAG_BAD_NODE;
+            continue;
+          }
+          const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
+          const float lp = X ? lprow[c] - a.row_lse[slot] : lprow[c];
+          const uint64_t x = candidate<G>(s, lp, tg, flat_base + (uint32_t)c, fl);
+          if (x != 0 && (uint32_t)(x >> 32) >= tau) e[ne++] = x;
+        }
+      }
+      block_append<4>(region, &cnt_s, e, ne);
+    }
+    __syncthreads();
+    n_out = cnt_s;
   } else if (live) {
     // ---- long rows: stream through the LDS buffer ----
     if (tid == 0) cnt_s = 0;
@@ -931,7 +970,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
   constexpr int NRG = 8;             // pool entries cached per thread (and per batch beyond)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ReqDesc rd = a.req[r];
-  const int W = rd.W, K = rd.K;
+  const int W = rd.W, K = keep_k(a, rd);
   const uint64_t* pool = a.pool + rd.pool_off;
 
   // beam prefix of the survivor counts, best live score
@@ -1196,7 +1235,7 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
   b.mask = nullptr;
   b.lprow = a.logprobs + (size_t)slot * a.C;
   b.beg = 0;
-  b.live = b.s != -INFINITY && !__builtin_isnan(b.s);
+  b.live = b.s != -INFINITY && !__builtin_isnan(b.s) && expands(a, slot, b.rd);
   if (__builtin_isnan(b.s)) fl |= GRW_FLAG_NAN_LOGPROB;
   if (b.live && !beam_row(a, slot, b.cnt, b.codes, &b.mask)) {
     fl |= GRW_FLAG_BAD_NODE;
@@ -1250,7 +1289,7 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   int n;
   int p = block_excl_scan<256>(na, red, &n);
   if (n == 0) return 0;
-  const int K = rd.K;
+  const int K = keep_k(a, rd);
   uint64_t* region = a.pool + rd.pool_off + (size_t)j * K;
   int32_t* redge = a.pool_edge + rd.pool_off + (size_t)j * K;
   // CSR edge of a survivor: position t + 256 k of a CSR row; in a dense row the rank of its
@@ -1352,7 +1391,7 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
   }
   int n;
   (void)block_excl_scan<NT>(na, red, &n);
-  const int K = rd.K;
+  const int K = keep_k(a, rd);
   auto key = [&](int k) -> uint32_t {
     const float kf = order_key<G>(s + lp[k], G ? tg[k] : 0.0f);
     return kf >= tau_f ? ordered_key(kf) : 0u;

@@ -14,11 +14,13 @@ import torch
 
 
 class DecodeLoop:
-    def __init__(self, ws, S: int, C: int, trie=None, device="cuda", overlap: bool = False):
+    def __init__(self, ws, S: int, C: int, trie=None, device="cuda", overlap: bool = False, fanout: bool = False):
         """ws: a bound Workspace; trie: (row_ptr, code, n_internal) device tensors, optionally
         followed by (dense_slot, dense_mask) for nodes with dense child masks, or None;
         overlap: run each layer's unshared stage on a side stream beside its shared stage
-        (beam_attn_decode_overlap) instead of the fused unshared + merge kernel."""
+        (beam_attn_decode_overlap) instead of the fused unshared + merge kernel; fanout: the
+        first step expands each request's prompt beam to its best W children (first-step
+        fan-out) instead of top_k."""
         from . import _lib  # noqa: F401  (the library must be loaded)
         self.ws, self.S, self.C = ws, S, C
         sumW = ws.sumW
@@ -32,6 +34,7 @@ class DecodeLoop:
         self.parents = torch.empty(S, sumW, dtype=torch.int32, device=dev)   # parent_idx
         self.sid = torch.empty(sumW, S, dtype=torch.int32, device=dev)
         self.side_stream = torch.cuda.Stream(device=dev) if overlap else None
+        self.fanout = fanout
 
     def select_step(self, d: int, logprobs, stream=None, noise=None, temperature: float = 0.0,
                     raw_logits: bool = False):
@@ -40,10 +43,11 @@ class DecodeLoop:
         with dense child masks (five-tuple) goes through beam_select_ex."""
         from . import beam_select, beam_select_ex, beam_select_gumbel, beam_select_logits
         cur, nxt = d % 2, (d + 1) % 2
-        if self.trie is not None and len(self.trie) > 3:
+        fan = self.fanout and d == 0
+        if fan or (self.trie is not None and len(self.trie) > 3):
             beam_select_ex(self.ws, logprobs, self.scores[cur], self.nodes[cur], self.trie, self.W, self.K, self.C,
                            self.tokens[d], self.parents[d], self.scores[nxt], self.nodes[nxt], noise, temperature,
-                           raw_logits, stream)
+                           raw_logits, stream, fan)
             return
         row_ptr, code, n_int = self.trie if self.trie is not None else (None, None, 0)
         if raw_logits:

@@ -311,6 +311,13 @@ typedef struct grw_select_opts {
   const float* noise;       /* Gumbel noise [sumW][C] (as for beam_select_gumbel) or NULL */
   float temperature;        /* with noise: finite, >= 0 */
   int32_t raw_logits;       /* 1: the input holds raw logits (as for beam_select_logits) */
+  int32_t first_step_fanout;  /* 1: first-step fan-out — only slot boff_r of each request
+                                 expands (the other slots are ignored) and it keeps its top
+                                 W_r candidates instead of top_k, so one prompt beam fills the
+                                 whole beam set; for the first step, from the level-0 state of
+                                 grw_beams_init.  A request wider than 2048 needs
+                                 C <= W_r * top_k_r (its prompt row then passes whole
+                                 through its pool); GRW_EUNSUPPORTED otherwise */
 } grw_select_opts;
 
 /*
@@ -318,8 +325,11 @@ typedef struct grw_select_opts {
  * struct; NULL for unconstrained selection), and opts (host struct; NULL for the
  * deterministic selection from log-probabilities).  beam_select, beam_select_gumbel and
  * beam_select_logits are this call with a CSR-only trie and the corresponding options;
- * results do not depend on which nodes have dense masks.  Arguments and errors otherwise
- * as for beam_select.
+ * results do not depend on which nodes have dense masks.  opts->first_step_fanout selects
+ * the first-step fan-out (FlashRec deployment guide, wide-beam section: the beam width sets
+ * the width of the fused expansion of the prompt, k x n rows): the one live prompt beam of
+ * each request is expanded to its best W_r children directly.  Arguments and errors
+ * otherwise as for beam_select.
  */
 int beam_select_ex(grw_ws* ws, const float* input, const float* beam_scores, const int32_t* beam_node,
                    const grw_trie* trie, const grw_select_opts* opts, int32_t W, int32_t K, int32_t C,

@@ -18,7 +18,9 @@ Readings where the pages are silent (each is the plainest one the rest supports)
 * a beam whose score is -inf is dead and contributes nothing; a beam with fewer than
   top_k valid children contributes all of them; a pool smaller than beam_width leaves
   pad slots (token -1, parent -1, score -inf) after all real slots;
-* at level 0 only slot 0 is live (score 0, empty prefix);
+* at level 0 only slot 0 is live (score 0, empty prefix); the first-step fan-out variant (the
+  prompt beam expanded to the full beam width, FlashRec deployment guide, wide-beam section)
+  is this selection with top_k = beam_width at level 0;
 * code c is valid for a beam with prefix p at level l iff p + (c,) is the length-(l+1)
   prefix of some catalog item (decided from the raw item list);
 * selection from raw logits (the fused variant): lse_b = float32(ln sum_c exp(x_bc)) over

@@ -41,18 +41,21 @@ def trie_device(trie, lib=None, C=None, dense_min_fanout=None):
 
 
 def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
-                          noise_of_step=None, temperature=0.0, raw_logits=False, dense_min_fanout=None):
+                          noise_of_step=None, temperature=0.0, raw_logits=False, dense_min_fanout=None,
+                          fanout=False):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
     every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
     the steps are the Gumbel-sampled selection at the given temperature; with raw_logits,
-    lp_of_step returns raw logits and the steps fuse their log-softmax.  Returns the loop."""
+    lp_of_step returns raw logits and the steps fuse their log-softmax; with fanout, the first
+    step is the first-step fan-out, whose oracle is the selection with top_k = W.  Returns
+    the loop."""
     Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
     R = len(Ws)
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
     trie = build_trie_csr(items, C) if items is not None else None
     psets = catalog_prefix_sets(items, C) if items is not None else None
     ws = make_ws(lib, Ws, Ks, [64] * R, C=C, S=S)
-    loop = lib.DecodeLoop(ws, S, C, trie_device(trie, lib, C, dense_min_fanout))
+    loop = lib.DecodeLoop(ws, S, C, trie_device(trie, lib, C, dense_min_fanout), fanout=fanout)
     ws.beams_init(loop.scores[0], loop.nodes[0])
     check = list(range(R)) if check is None else list(check)
     state = {r: initial_beams(Ws[r]) for r in check}
@@ -72,7 +75,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
             a, W = boff[r], Ws[r]
             scores, prefixes = state[r]
             sel = oracle_select_logits if raw_logits else oracle_select
-            res = sel(lp[a:a + W], scores, prefixes, d, Ks[r], W, C, psets,
+            res = sel(lp[a:a + W], scores, prefixes, d, W if fanout and d == 0 else Ks[r], W, C, psets,
                       None if g is None else g[a:a + W], temperature)
             where = f"{label} step {d} request {r}"
             np.testing.assert_array_equal(tok[a:a + W], res["tokens"], err_msg=where + " tokens")
@@ -90,7 +93,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
             assert np.all(nd[a + n:a + W] == -1), where
             # the kept pool holds every winner and at most W * K entries
             pool = ws.pool_size(r)
-            assert n <= pool <= W * Ks[r], f"{where}: pool {pool} for {n} winners"
+            assert n <= pool <= W * (W if fanout and d == 0 else Ks[r]), f"{where}: pool {pool} for {n} winners"
             pools.setdefault(r, []).append(pool)
             state[r] = (res["scores"], res["prefixes"])
     flags = ws.error_flags()

@@ -16,6 +16,10 @@ the Gumbel-max law: with one live beam and W = K = 1 the selected code is distri
 softmax(lp / T) (chi-square over 20 000 draws); G4 the returned scores hold no noise and the
 outputs are ordered by the perturbed key.
 
+First-step fan-out: F1 at level 0 (one live prompt beam) the selection with top_k = W is the
+textbook top-W of that beam's valid codes by (key descending, code ascending), pads after;
+with top_k < W the plain first step keeps only top_k of them.
+
 Selection from raw logits: L1 the row lse equals scipy's logsumexp rounded to float32, and
 exp(lp) sums to 1; L2 with logits that already are log-probabilities rounded from a float64
 log-softmax, the lse is ~0 and the selection matches the log-probability oracle up to the
@@ -176,6 +180,31 @@ def test_k_at_least_fanout_is_global_topw():
             assert np.array_equal(res["tokens"][:n], flats[order] % C)
             assert np.all(res["parents"][n:] == -1)
             scores, prefixes = res["scores"], res["prefixes"]
+
+
+def test_first_step_fanout_is_top_w_of_the_prompt_row():
+    rng = np.random.default_rng(17)
+    for _ in range(300):
+        W, C, L = int(rng.integers(1, 40)), int(rng.integers(2, 64)), 3
+        items = np.unique(rng.integers(0, C, size=(int(rng.integers(1, 300)), L)), axis=0)
+        psets = catalog_prefix_sets(items, C)
+        scores, prefixes = initial_beams(W)
+        lp = rng.choice(np.array([0.0, -0.5, -0.5, -1.0, -2.0, -np.inf], np.float32), size=(W, C))
+        res = oracle_select(lp, scores, prefixes, 0, W, W, C, psets)
+        valid = sorted(set(int(p) for p in psets[1].tolist()))
+        keys = np.array([np.float32(0.0) + lp[0, c] for c in valid], np.float32)
+        codes = np.array(valid)
+        keep = keys != -np.inf
+        keys, codes = keys[keep], codes[keep]
+        order = np.lexsort((codes, -keys))[:W]
+        n = order.size
+        assert np.array_equal(res["tokens"][:n], codes[order])
+        assert np.all(res["parents"][:n] == 0) and np.all(res["parents"][n:] == -1)
+        assert np.all(res["tokens"][n:] == -1)
+        K = max(1, W // 3)
+        plain = oracle_select(lp, scores, prefixes, 0, K, W, C, psets)
+        assert int((plain["parents"] >= 0).sum()) == min(K, n)
+        assert np.array_equal(plain["tokens"][:min(K, n)], codes[order][:min(K, n)])
 
 
 def test_width_one_is_constrained_argmax():
