@@ -146,3 +146,53 @@ def test_stage_by_stage_equals_fused_path(lib):
                         {0: range(int(W[0])), 7: range(int(W[7]))}, TOL["bf16"], label="stagewise")
     with pytest.raises(lib.GrwError):
         lib.beam_attn_decode_stages(ws, *args, out_b, 0)
+
+
+def test_wide_and_narrow_requests_equal_stagewise(lib):
+    """Wide bf16 requests (the 8-wave shared-stage kernel) next to a narrow one (the 4-wave
+    kernel), with split and unsplit prompts, deep ancestry and dead slots: the default path
+    equals the stage-by-stage path, matches the oracle, and repeats bit for bit over calls
+    at other depths and over graph replays."""
+    import dataclasses
+    wl = dataclasses.replace(workload("qwen06b"), n_requests=3, W=None, K=None, P=None, S=4, index=97)
+    Ws = np.array([300, 40, 129], np.int32)
+    Ps = np.array([3000, 200, 64], np.int32)
+    Ks = Ws.copy()
+    layer = attention_layer(wl, 0, shapes=(Ws, Ks, Ps))
+    par = random_parents(wl, shapes=(Ws, Ks, Ps), dead_frac=0.15)
+    ws = make_ws(lib, Ws, Ks, Ps, C=16, S=wl.S)
+    assert ws.splits(0) > 1 and ws.splits(2) == 1
+    dev = upload_layer(layer, wl.q_dtype, wl.kv_dtype)
+    parents = torch.from_numpy(par).cuda()
+    rng = np.random.default_rng(6)
+    outs = {}
+    for d in (3, 0, 2):
+        out_a = torch.full((int(Ws.sum()), wl.Hq, wl.D), float("nan"), device="cuda")
+        out_b = torch.full_like(out_a, float("nan"))
+        args = (dev["q"][d], dev["k_s"], dev["v_s"], None, None, dev["k_u"], dev["v_u"], parents, d)
+        lib.beam_attn_decode(ws, *args, out_a)
+        for mask in (lib.STAGE_SHARED, lib.STAGE_UNSHARED, lib.STAGE_MERGE):
+            lib.beam_attn_decode_stages(ws, *args, out_b, mask)
+        torch.cuda.synchronize()
+        a, b = out_a.cpu().numpy(), out_b.cpu().numpy()
+        assert np.all(np.isfinite(a))
+        assert np.max(np.abs(a - b)) <= 1e-5, f"d={d}: {np.max(np.abs(a - b))}"
+        samples = {r: rng.choice(int(Ws[r]), size=min(24, int(Ws[r])), replace=False) for r in range(3)}
+        err = attention_vs_oracle(a, layer, par, d, list(Ws), wl.q_dtype, wl.kv_dtype, samples, TOL["bf16"],
+                                  label=f"wide + narrow d={d}")
+        say(f"[attn] wide + narrow d={d}: vs stage-wise {np.max(np.abs(a - b)):.2e}, oracle {err:.3e}")
+        outs[d] = out_a.clone()
+    # repeated calls inside a graph, replayed twice
+    out_g = torch.empty_like(outs[3])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for d in (0, 3):
+            lib.beam_attn_decode(ws, dev["q"][d], dev["k_s"], dev["v_s"], None, None, dev["k_u"], dev["v_u"],
+                                 parents, d, out_g)
+    for _ in range(2):
+        out_g.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, outs[3])
+    assert ws.error_flags() == 0
