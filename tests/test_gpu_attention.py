@@ -97,6 +97,19 @@ def test_ultra5000_deep_ancestry(lib):
     run_attention(lib, wl, layer, par, W, K, P, [0, 7, 15], samples)
 
 
+def test_deepest_ancestry(lib):
+    """The deepest decode step the library takes (step 63 of 64): every slot walks 63 parent
+    pointers; bf16 (8-wave kernel for the wide request) and the narrow request."""
+    import dataclasses
+    wl = dataclasses.replace(workload("qwen06b"), n_requests=2, W=None, K=None, P=None, S=64, index=98)
+    Ws = np.array([80, 6], np.int32)
+    Ps = np.array([200, 64], np.int32)
+    Ks = Ws.copy()
+    layer = attention_layer(wl, 0, shapes=(Ws, Ks, Ps))
+    par = random_parents(wl, shapes=(Ws, Ks, Ps), dead_frac=0.1)
+    run_attention(lib, wl, layer, par, Ws, Ks, Ps, [63, 31], all_slots(Ws))
+
+
 @pytest.mark.parametrize("P", [1, 63, 65, 1000, 4097])
 def test_ragged_prompt_lengths_and_rows(lib, P):
     """Prompt lengths off the 64-key tile, row counts off the 128-row tile, split prompts."""

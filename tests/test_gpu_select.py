@@ -49,6 +49,18 @@ def test_wide_requests_beyond_the_fused_limit(lib):
     select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wide-multi")
 
 
+def test_maximum_width(lib):
+    """The largest beam width the library takes (8192): the first step fans the prompt beam
+    out to 4096 children, the next fills all 8192 slots from the 4096 x 2 pool."""
+    rng = np.random.default_rng(8)
+    W, K, C, S = [8192], [2], 4096, 2
+    lps = [rng.normal(0.0, 2.0, size=(sum(W), C)) for _ in range(S)]
+    lps = [np.minimum((x - np.log(np.exp(x).sum(axis=1, keepdims=True))).astype(np.float32), 0.0) for x in lps]
+    say("[select] W = 8192")
+    loop, ws = select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="w8192", fanout=True)
+    assert int((loop.parents[1] >= 0).sum().item()) == 8192
+
+
 def test_mixed_ragged_batch(lib):
     wl = workload("mixed_fp8")
     W, K, P = request_shapes(wl)
