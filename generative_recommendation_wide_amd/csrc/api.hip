@@ -312,9 +312,10 @@ int grw_ws_destroy(grw_ws* w) {
   return GRW_OK;
 }
 
-int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32_t* K_host,
-                      const int32_t* P_host, void* stream) {
-  if (!w || !W_host || !K_host || !P_host) return GRW_EINVAL;
+namespace {
+
+int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32_t* K_host, const int32_t* P_host,
+               void* stream) {
   const grw_limits& L = w->lim;
   if (n_requests < 1 || n_requests > L.max_requests) return GRW_EINVAL;
   std::vector<ReqDesc> req(n_requests);
@@ -400,6 +401,19 @@ int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, cons
   w->maxK = maxK;
   w->bound = true;
   return GRW_OK;
+}
+
+}  // namespace
+
+int grw_ws_bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32_t* K_host,
+                      const int32_t* P_host, void* stream) {
+  if (!w || !W_host || !K_host || !P_host) return GRW_EINVAL;
+  try {
+    return bind_batch(w, n_requests, W_host, K_host, P_host, stream);
+  } catch (const std::bad_alloc&) {   // host work lists of the bind
+    w->bound = false;
+    return GRW_ENOMEM;
+  }
 }
 
 int grw_beams_init(grw_ws* w, float* beam_scores, int32_t* beam_node, void* stream) {
@@ -643,15 +657,21 @@ int grw_plan_batches(int32_t n, const int32_t* W, int32_t slot_budget, int32_t m
   // Max tree over batches 0..n-1 (at most n open): a leaf holds the batch's free rows, or -1
   // once it holds max_requests requests.  Unopened batches hold the whole budget, so the
   // leftmost leaf with room for a request is an open batch or the next one to open.
-  int32_t size = 1;
+  int64_t size = 1;
   while (size < n) size <<= 1;
-  std::vector<int32_t> tree(2 * (size_t)size, slot_budget), count(n, 0);
+  std::vector<int32_t> tree, count;
+  try {
+    tree.assign(2 * (size_t)size, slot_budget);
+    count.assign((size_t)n, 0);
+  } catch (const std::bad_alloc&) {
+    return GRW_ENOMEM;
+  }
   int32_t opened = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t w = W[i];
-    int32_t v = 1;
+    int64_t v = 1;
     while (v < size) v = tree[2 * v] >= w ? 2 * v : 2 * v + 1;
-    const int32_t b = v - size;    // b <= opened <= i < n: batch `opened` is still empty
+    const int32_t b = (int32_t)(v - size);   // b <= opened <= i < n: batch `opened` is still empty
     batch_of[i] = b;
     opened = std::max(opened, b + 1);
     const int32_t rows = tree[v] - w;

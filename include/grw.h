@@ -57,7 +57,8 @@ typedef struct grw_ws grw_ws;
 enum grw_status {
   GRW_OK = 0,
   GRW_EINVAL = 1,        /* bad argument (null pointer, size beyond a limit, mismatch)  */
-  GRW_ENOMEM = 2,        /* device or pinned-host allocation failed in grw_ws_create     */
+  GRW_ENOMEM = 2,        /* an allocation failed (device or pinned host memory in
+                            grw_ws_create; host memory in the host-side calls)            */
   GRW_EDEVICE = 3,       /* a HIP runtime call failed                                    */
   GRW_EUNSUPPORTED = 4,  /* valid but unsupported shape / dtype combination              */
   GRW_ESTATE = 5         /* call order: e.g. a step call before grw_ws_bind_batch        */
@@ -361,7 +362,8 @@ int grw_trie_dense_build(const int32_t* row_ptr, const int32_t* code, int32_t n_
  *   batch_of  [n] int32 host, written: batch index of each request
  *   n_batches int32 host, written: the number of batches (0 for n == 0)
  * GRW_EINVAL for n < 0, NULL pointers (W and batch_of may be NULL when n == 0),
- * slot_budget < 1, max_requests < 1, or a width outside [1, slot_budget].  O(n log n).
+ * slot_budget < 1, max_requests < 1, or a width outside [1, slot_budget]; GRW_ENOMEM when
+ * its host working memory (about 12 bytes per request) cannot be allocated.  O(n log n).
  */
 int grw_plan_batches(int32_t n, const int32_t* W, int32_t slot_budget, int32_t max_requests,
                      int32_t* batch_of, int32_t* n_batches);
