@@ -528,7 +528,7 @@ def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
             "live_beams": live, "bytes_per_call": bytes_, "avg_call_us": round(t * 1e6, 2),
             "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
             "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
-            "kernels": "select_pilot_kernel + select_beam_kernel + select_final_kernel",
+            "kernels": "select_pilot_beam_kernel + select_final_kernel",
             "entry_point": ("beam_select_logits" if raw_logits else "beam_select_gumbel" if temperature is not None
                             else "beam_select") + ("" if temperature is None else f" (temperature {temperature})"),
             "unfused_log_softmax_then_select_us": None if unfused is None else round(unfused, 2)}

@@ -84,6 +84,11 @@ class Workspace:
         _lib.check("grw_ws_pool_size", _L.grw_ws_pool_size(self.handle, r, _stream(stream), ctypes.byref(v)))
         return v.value
 
+    def set_wait_limit(self, polls: int) -> None:
+        """Polls a beam workgroup of the fused selection makes for its bound before it goes on
+        without one (same result, slower); 0 forces that fallback."""
+        _lib.check("grw_ws_set_wait_limit", _L.grw_ws_set_wait_limit(self.handle, int(polls)))
+
     def error_flags(self, stream=None) -> int:
         v = ctypes.c_int32()
         _lib.check("grw_ws_error", _L.grw_ws_error(self.handle, _stream(stream), ctypes.byref(v)))

@@ -39,6 +39,7 @@ struct grw_ws {
   float* d_row_lse = nullptr;       // [max_total_beams] row lse of the selection from raw logits
   uint64_t* d_pilot_buf = nullptr;
   uint32_t* d_step_state = nullptr;    // [max_requests]: pilots finished in the current step
+  uint64_t* d_sync = nullptr;          // [max_requests][kSyncCopies * kSyncStride] step-state words
   int32_t* d_flags = nullptr;
   // fork and join events of the two-stream attention
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -54,6 +55,7 @@ struct grw_ws {
   int n_wide = 0;                // leading items of the work list that use the 8-wave kernel
   int n_pilots = 0;              // pilot workgroups of the deterministic selection
   int n_pilots_s = 0;            // pilot workgroups of the sampled selection
+  int32_t wait_limit = kBoundSpin;   // polls of a beam workgroup waiting for its bound
   std::vector<ReqDesc> req;
 };
 
@@ -95,6 +97,7 @@ void free_all(grw_ws* w) {
   (void)hipFree(w->d_pilot_desc);
   (void)hipFree(w->d_row_lse);
   (void)hipFree(w->d_step_state);
+  (void)hipFree(w->d_sync);
   (void)hipFree(w->d_pilot_buf);
   (void)hipFree(w->d_flags);
   if (w->h_stage) (void)hipHostFree(w->h_stage);
@@ -275,6 +278,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 8 * B);
   if (st == GRW_OK) st = dev_alloc(&w->d_row_lse, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_step_state, (int64_t)L.max_requests);
+  if (st == GRW_OK) st = dev_alloc(&w->d_sync, (int64_t)L.max_requests * kSyncCopies * kSyncStride);
   if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
   if (st == GRW_OK) {
@@ -291,6 +295,7 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) {
     if (hipMemset(w->d_bound, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
         hipMemset(w->d_step_state, 0, sizeof(uint32_t) * L.max_requests) != hipSuccess ||
+        hipMemset(w->d_sync, 0, sizeof(uint64_t) * L.max_requests * kSyncCopies * kSyncStride) != hipSuccess ||
         hipMemset(w->d_flags, 0, sizeof(int32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess)
       st = GRW_EDEVICE;
@@ -579,6 +584,8 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   a.n_pilots = noise != nullptr ? w->n_pilots_s : w->n_pilots;
   a.pilot_buf = w->d_pilot_buf;
   a.pilot_count = w->d_step_state;
+  a.sync = w->d_sync;
+  a.wait_limit = w->wait_limit;
   a.out_token = out_token;
   a.out_parent = out_parent;
   a.out_score = out_score;
@@ -736,6 +743,12 @@ int grw_ws_pool_size(grw_ws* w, int32_t r, void* stream, int64_t* pool_size) {
   for (int32_t c : cnt) n += c;
   *pool_size = n;
   return hip_status(e);
+}
+
+int grw_ws_set_wait_limit(grw_ws* w, int32_t polls) {
+  if (!w || polls < 0) return GRW_EINVAL;
+  w->wait_limit = polls;
+  return GRW_OK;
 }
 
 int grw_ws_splits(const grw_ws* w, int32_t r, int32_t* n_splits) {

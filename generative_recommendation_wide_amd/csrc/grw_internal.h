@@ -46,6 +46,9 @@ constexpr int kRegC = 32;          // candidates per thread of the one-pass per-
 constexpr int kOnePass = 256 * kRegC;   // rows up to this length take the one-pass path
 constexpr int kMaxPilots = 64;     // pilot beams per request
 constexpr int kPilotCap = 4096;    // pilot candidates per request
+constexpr int kSyncCopies = 32;    // copies of a request's step-state word (spread polling)
+constexpr int kSyncStride = 32;    // words between copies (256 bytes)
+constexpr int kBoundSpin = 1 << 18;   // default polls of a beam workgroup waiting for its bound
 constexpr int kHistBins = 4096;    // survivor histogram bins of the global select
 constexpr int kBinCap = 1024;      // largest histogram bin the global select ranks in place
 
@@ -100,6 +103,11 @@ struct SelArgs {
   int32_t n_pilots;
   uint64_t* pilot_buf;      // [R][kPilotCap] pilot candidates
   uint32_t* pilot_count;    // [R] pilots finished this step
+  int32_t wait_limit;       // polls before a waiting beam workgroup proceeds without the bound
+  uint64_t* sync;           // [R][kSyncCopies] words kSyncStride apart: the request's step
+                            //     word for beam workgroups that wait inside the pilot +
+                            //     per-beam kernel (top bit: the bound, in the low 32 bits, is
+                            //     published); cleared by the W-of-pool stage
   int32_t* out_token;
   int32_t* out_parent;
   float* out_score;

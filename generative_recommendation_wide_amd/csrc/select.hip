@@ -24,6 +24,11 @@
 //   when more remain.  Longer rows stream through an LDS buffer that a radix select trims
 //   to top_k whenever it fills.  A beam that alone holds >= W_r survivors raises the bound
 //   to its own W_r-th best.
+// On the register-resident path (rows of at most 8192 codes, W <= 1024) the pilots and the
+// per-beam stage share one launch (select_pilot_beam): the pilots are its first
+// workgroups, and the beam workgroups read their rows at once and wait for the bound, which
+// the request's last pilot publishes in a step word; the W-of-pool stage follows as
+// select_final.
 // select_global: one workgroup per request.  The beams' survivor counts give every entry a
 //   place in one index range.  A histogram of the entries' keys (bins measured down from
 //   the best live score) finds the bin that holds the W_r-th best entry; the entries of
@@ -537,6 +542,21 @@ __device__ __forceinline__ uint32_t row_key(const RowRegs<L, G>& rr, int k, int 
   return o >= tau ? o : 0u;
 }
 
+// The best candidate of a loaded row of up to kOnePass candidates (0 when none).
+template <int L, bool G, bool X>
+__device__ __forceinline__ uint64_t loaded_row_best(RowRegs<L, G>& rr, const SelArgs& a, int slot, const float* lprow,
+                                                    int cnt, float s, uint32_t flat_base, int& fl, float* redf,
+                                                    double* redd) {
+  if constexpr (X) to_logprobs<L, G>(rr, a, slot, lprow, a.lse_ready == 0, redf, redd, fl);
+  uint64_t best = 0;
+#pragma unroll
+  for (int k = 0; k < kRegC; ++k) {
+    const uint32_t o = row_key<L>(rr, k, cnt, s, 0u, fl);
+    if (o) best = max(best, composite_key(o, flat_base + (uint32_t)rr.code_of(k)));
+  }
+  return best;
+}
+
 // The best candidate of a row of up to kOnePass candidates (0 when none).
 template <int L, bool G, bool X>
 __device__ __forceinline__ uint64_t row_best(const SelArgs& a, int slot, const float* lprow, const float* grow,
@@ -585,6 +605,9 @@ __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
 // wait until this thread's stores are acknowledged at device scope
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Step-state word: bit 63 set once the request's bound (low 32 bits) is published.
+constexpr uint64_t kSyncBound = 1ull << 63;
+
 // Candidates a beam keeps: top_k, or at a first-step fan-out the request's beam width.  A
 // fan-out wider than the per-beam selection holds (kMaxK) keeps every candidate instead,
 // up to the request's whole pool region (W_r * K_r entries, at least the row length), and
@@ -605,30 +628,54 @@ __device__ __forceinline__ bool expands(const SelArgs& a, int slot, const ReqDes
 // top_k of its beam) with device-coherent stores and counts itself; the request's last
 // pilot sets bound[r] to the W_r-th best key of all contributions (0 when there are fewer
 // than W_r) and resets the count.
-template <bool G, bool X>
-__global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
-  __shared__ uint64_t red64[4];
-  __shared__ float redf[4];
-  __shared__ double redd[4];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scr[4];
-  __shared__ uint32_t red32[8];
-  __shared__ int red[4];
-  __shared__ int last_s;
+struct PilotLds {
+  uint64_t red64[4];
+  float redf[4];
+  double redd[4];
+  uint32_t hist[256];
+  uint32_t scr[4];
+  uint32_t red32[8];
+  int red[4];
+  int last;
+};
+
+// Pilot workgroup `pi`.  PUBLISH (pilots inside the per-beam kernel): the request's last
+// pilot stores the bound with a device-coherent store and, once that store is acknowledged,
+// sets the request's ready word that the kernel's beam workgroups wait on.
+// LT >= 0: every row of the launch has that layout and fits the one-read path.
+template <bool G, bool X, bool PUBLISH, int LT = -1>
+__device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S) {
+  uint64_t* red64 = S.red64;
+  float* redf = S.redf;
+  double* redd = S.redd;
+  uint32_t* hist = S.hist;
+  uint32_t* scr = S.scr;
+  uint32_t* red32 = S.red32;
+  int* red = S.red;
+  int& last_s = S.last;
   const int tid = threadIdx.x;
-  const int4 pd = ((const int4*)a.pilot_desc)[blockIdx.x];
+  const int4 pd = ((const int4*)a.pilot_desc)[pi];
   const int slot = pd.x, r = pd.y, gsz = pd.w;
-  const ReqDesc rd = a.req[r];
-  const float s = a.scores[slot];
-  const uint32_t flat_base = (uint32_t)(slot - rd.boff) * (uint32_t)a.C;
   const float* lprow = a.logprobs + (size_t)slot * a.C;
   const float* grow = G ? a.noise + (size_t)slot * a.C : nullptr;
   int cnt = a.C, fl = 0;
+  // full rows: the row loads go out before the descriptor loads (a dead beam's row is read
+  // and ignored)
+  constexpr bool kEarly = LT == kFull || LT == kFullScalar;
+  RowRegs<kEarly ? LT : kFull, G> rr0;
+  if constexpr (kEarly) load_row<LT, G>(rr0, a, lprow, grow, nullptr, cnt, fl);
+  const ReqDesc rd = a.req[r];
+  const float s = a.scores[slot];
+  const uint32_t flat_base = (uint32_t)(slot - rd.boff) * (uint32_t)a.C;
   const int32_t* codes = nullptr;
   uint64_t best = 0;
   const uint32_t* mask = nullptr;
   if (s != -INFINITY && !__builtin_isnan(s) && expands(a, slot, rd) && beam_row(a, slot, cnt, codes, &mask)) {
-    if (cnt <= kOnePass) {
+    if constexpr (kEarly) {
+      best = loaded_row_best<LT, G, X>(rr0, a, slot, lprow, cnt, s, flat_base, fl, redf, redd);
+    } else if constexpr (LT >= 0) {
+      if (cnt <= kOnePass) best = row_best<LT, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd, mask);
+    } else if (cnt <= kOnePass) {
       const int lay = row_layout(a, codes, lprow);
       if (lay == kFull) best = row_best<kFull, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
       else if (lay == kFullScalar)
@@ -678,10 +725,27 @@ __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   uint32_t lo = 0;
   if (nv >= rd.W)
     lo = regs_select32<256, NP>([&](int k) { return pk[k]; }, (uint32_t)rd.W, (uint32_t)nv, hist, scr, red32).v;
-  if (tid == 0) {
+  if constexpr (PUBLISH) {
+    // the bound in every copy of the step word, after the bound itself is stored for the
+    // W-of-pool stage (beam workgroups raise it only after they have read the word)
+    if (tid == 0) {
+      st_dev(&a.bound[r], lo);
+      st_dev(&a.pilot_count[r], 0u);
+      wait_stores();
+    }
+    __syncthreads();
+    if (tid < kSyncCopies)
+      st_dev(&a.sync[((size_t)r * kSyncCopies + tid) * kSyncStride], kSyncBound | lo);
+  } else if (tid == 0) {
     a.bound[r] = lo;
     a.pilot_count[r] = 0u;
   }
+}
+
+template <bool G, bool X>
+__global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
+  __shared__ PilotLds S;
+  pilot_run<G, X, false>(a, blockIdx.x, S);
 }
 
 // --------------------------------------------------------------------------------------
@@ -1202,10 +1266,9 @@ __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) 
 // --------------------------------------------------------------------------------------
 // register-resident step: per-beam stage, then the W-of-pool stage
 // --------------------------------------------------------------------------------------
-// Used when every row fits the one-read path (C <= kOnePass) and W <= kFusedMaxW, after
-// select_pilot has set the bounds.  The per-beam kernel runs one small workgroup per beam
-// slot (few registers and no large LDS arrays, so every slot of a wide batch is resident
-// at once); the W-of-pool kernel runs one 1024-thread workgroup per request.
+// Used when every row fits the one-read path (C <= kOnePass) and W <= kFusedMaxW.  The
+// pilot + per-beam kernel runs one small workgroup per pilot and per beam slot (no large
+// LDS arrays); the W-of-pool kernel runs one 1024-thread workgroup per request.
 constexpr int kFusedMaxW = 1024;
 constexpr int kFusedBins = 1024;
 constexpr int kFusedBinCap = 512;
@@ -1223,13 +1286,15 @@ struct BeamRow {
   const float* lprow;
 };
 
-__device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& fl) {
+// read_bound: false when the bound is published during the same kernel (the caller then
+// waits for it and sets b.tau; no plain load may cache the word before that)
+__device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& fl, bool read_bound = true) {
   BeamRow b;
   b.slot = slot;
   b.r = a.slot_req[slot];
   b.s = a.scores[slot];
   b.rd = a.req[b.r];           // descriptor and bound are read before the row
-  b.tau = a.bound[b.r];
+  b.tau = read_bound ? a.bound[b.r] : 0u;
   b.cnt = a.C;
   b.codes = nullptr;
   b.mask = nullptr;
@@ -1419,31 +1484,64 @@ __device__ __forceinline__ void overflow_row(const SelArgs& a, const ReqDesc& rd
   if (tid == 0) st_dev(&a.surv_count[slot], min(total, K));
 }
 
-// Per-beam stage: survivors of each beam slot (candidates >= the request's bound) into the
-// slot's pool region, and the slot's survivor count (-1: more than top_k without noise,
-// left to the W-of-pool stage).
-template <int L, bool G, bool X>
-__global__ __launch_bounds__(256) void select_beam_kernel(SelArgs a) {
-  __shared__ int red[4];
-  __shared__ uint32_t mwords[L == kTrie ? 256 : 1];   // dense row: its child mask, and
-  __shared__ uint32_t mprefix[L == kTrie ? 256 : 1];  // the children before each word
-  __shared__ float redf[X ? 4 : 1];
-  __shared__ double redd[X ? 4 : 1];
-  __shared__ uint32_t hist[G ? 256 : 1];
-  __shared__ uint32_t scr[4];
-  __shared__ uint32_t red32[8];
-  const int tid = threadIdx.x;
-  const int slot = blockIdx.x;
-  int fl = 0;
-  const BeamRow b = beam_setup(a, slot, fl);
-  RowRegs<L, G> rr;
-  if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl, b.mask);
-  if constexpr (X) {
-    // pilot slots' lse came from the pilot kernel; the others are computed here
-    const bool pilot = b.slot - b.rd.boff < (G ? b.rd.n_pilot_s : b.rd.n_pilot);
-    if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, !pilot, redf, redd, fl);
+// The per-beam stage with the pilots in the same launch.  Workgroups [0, n_pilots) are the
+// pilots and never wait; every later workgroup takes one beam slot, issues its row loads,
+// and then waits until its request's last pilot has published the bound.  Workgroups are
+// dispatched in index order, so every pilot is resident or finished before a workgroup
+// that waits for it starts, and the waiting workgroups' row loads overlap the pilots'
+// work.  The wait is bounded: after a.wait_limit polls the workgroup proceeds with bound 0,
+// which admits every candidate and leaves its row to the overflow path (slower, same
+// result).
+//
+// Thread 0 polls its copy of request r's step word until `bit` is set (at most
+// a.wait_limit polls); every thread gets the last value read.
+__device__ __forceinline__ uint64_t wait_sync(const SelArgs& a, int r, uint64_t bit, uint64_t* word) {
+  if (threadIdx.x == 0) {
+    const uint64_t* p = &a.sync[((size_t)r * kSyncCopies + blockIdx.x % kSyncCopies) * kSyncStride];
+    uint64_t v = 0;
+    for (int i = 0; i < a.wait_limit; ++i) {
+      v = ld_dev(p);
+      if (v & bit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *word = v;
   }
-  const int n_out = keep_beam<L, G>(a, b, rr, fl, red, hist, scr, red32, mwords, mprefix);
+  __syncthreads();
+  const uint64_t v = *word;
+  __syncthreads();
+  return v;
+}
+
+template <int L, bool G, bool X>
+__global__ __launch_bounds__(256) void select_pilot_beam_kernel(SelArgs a) {
+  __shared__ PilotLds S;
+  __shared__ uint32_t mwords[L == kTrie ? 256 : 1];
+  __shared__ uint32_t mprefix[L == kTrie ? 256 : 1];
+  __shared__ uint64_t word_s;
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < a.n_pilots) {
+    pilot_run<G, X, true, L>(a, blockIdx.x, S);
+    return;
+  }
+  const int slot = blockIdx.x - a.n_pilots;
+  int fl = 0;
+  RowRegs<L, G> rr;
+  int lfl = 0;
+  if constexpr (L != kTrie)    // full rows: loads before the descriptor loads, kept if the beam is live
+    load_row<L, G>(rr, a, a.logprobs + (size_t)slot * a.C, G ? a.noise + (size_t)slot * a.C : nullptr, nullptr, a.C, lfl);
+  BeamRow b = beam_setup(a, slot, fl, false);
+  if constexpr (L == kTrie) {
+    if (b.live) load_row<L, G>(rr, a, b.lprow, G ? a.noise + (size_t)slot * a.C : nullptr, b.codes, b.cnt, fl, b.mask);
+  } else if (b.live) {
+    fl |= lfl;
+  }
+  const uint64_t w = wait_sync(a, b.r, kSyncBound, &word_s);
+  b.tau = (w & kSyncBound) ? (uint32_t)w : 0u;
+  // every slot computes its own row lse (a pilot slot's equals its pilot's: same layout, same
+  // reduction order)
+  if constexpr (X)
+    if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, true, S.redf, S.redd, fl);
+  const int n_out = keep_beam<L, G>(a, b, rr, fl, S.red, S.hist, S.scr, S.red32, mwords, mprefix);
   if (tid == 0) a.surv_count[slot] = n_out;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
@@ -1481,6 +1579,7 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, L);
   __syncthreads();
   if (threadIdx.x == 0) a.bound[r] = 0u;
+  if (threadIdx.x < kSyncCopies) a.sync[((size_t)r * kSyncCopies + threadIdx.x) * kSyncStride] = 0ull;
 }
 
 // Row lse of every live beam slot for the general kernels (rows of any length, read with
@@ -1599,15 +1698,14 @@ hipError_t select_fused_path(const SelArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  select_pilot_kernel<G, X><<<a.n_pilots, 256, 0, s>>>(a);
-  const int grid = a.sumW;
+  const int grid = a.n_pilots + a.sumW;     // pilots first, then one workgroup per slot
   const bool aligned = (((uintptr_t)a.logprobs) & 15) == 0 && (!G || (((uintptr_t)a.noise) & 15) == 0);
   if (a.row_ptr != nullptr)
-    select_beam_kernel<kTrie, G, X><<<grid, 256, 0, s>>>(a);
+    select_pilot_beam_kernel<kTrie, G, X><<<grid, 256, 0, s>>>(a);
   else if ((a.C & 3) == 0 && aligned)
-    select_beam_kernel<kFull, G, X><<<grid, 256, 0, s>>>(a);
+    select_pilot_beam_kernel<kFull, G, X><<<grid, 256, 0, s>>>(a);
   else
-    select_beam_kernel<kFullScalar, G, X><<<grid, 256, 0, s>>>(a);
+    select_pilot_beam_kernel<kFullScalar, G, X><<<grid, 256, 0, s>>>(a);
   select_final_kernel<G, X><<<a.R, kFinThreads, sizeof(FinLds), s>>>(a);
   return hipGetLastError();
 }

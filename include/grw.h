@@ -392,6 +392,16 @@ int grw_ws_splits(const grw_ws* ws, int32_t r, int32_t* n_splits);
    the stream, then writes the count to *pool_size (host pointer).  Diagnostics only. */
 int grw_ws_pool_size(grw_ws* ws, int32_t r, void* stream, int64_t* pool_size);
 
+/* Bound on how long a beam workgroup of the fused pilot + per-beam selection kernel polls
+   for its request's bound (the kernel used when every row has at most 8192 codes and
+   W <= 1024): at most `polls` polls (default 262144, a fraction of a second).  A workgroup
+   that gives up proceeds with no bound: it admits every candidate of its row and leaves a
+   row with more than top_k of them to the W-of-pool stage, so the result is the same, only
+   slower.  For tests of that fallback (polls = 0 forces it) and for callers that want a
+   tighter bound on the wait.  Host-side; affects later beam_select* calls on this
+   workspace.  GRW_EINVAL if polls < 0. */
+int grw_ws_set_wait_limit(grw_ws* ws, int32_t polls);
+
 const char* grw_status_str(int status);
 
 #ifdef __cplusplus

@@ -42,19 +42,21 @@ def trie_device(trie, lib=None, C=None, dense_min_fanout=None):
 
 def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
                           noise_of_step=None, temperature=0.0, raw_logits=False, dense_min_fanout=None,
-                          fanout=False):
+                          fanout=False, wait_limit=None):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
     every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
     the steps are the Gumbel-sampled selection at the given temperature; with raw_logits,
     lp_of_step returns raw logits and the steps fuse their log-softmax; with fanout, the first
-    step is the first-step fan-out, whose oracle is the selection with top_k = W.  Returns
-    the loop."""
+    step is the first-step fan-out, whose oracle is the selection with top_k = W; with
+    wait_limit, the workspace's bound-wait limit.  Returns the loop."""
     Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
     R = len(Ws)
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
     trie = build_trie_csr(items, C) if items is not None else None
     psets = catalog_prefix_sets(items, C) if items is not None else None
     ws = make_ws(lib, Ws, Ks, [64] * R, C=C, S=S)
+    if wait_limit is not None:
+        ws.set_wait_limit(wait_limit)
     loop = lib.DecodeLoop(ws, S, C, trie_device(trie, lib, C, dense_min_fanout), fanout=fanout)
     ws.beams_init(loop.scores[0], loop.nodes[0])
     check = list(range(R)) if check is None else list(check)

@@ -124,3 +124,35 @@ def test_wide_tie_plateau(lib):
     C = 700
     lps = [np.full((300, C), -1.0, np.float32) for _ in range(2)]
     select_loop_vs_oracle(lib, [300], [250], C, 2, lambda d: lps[d], None, label="plateau")
+
+
+@pytest.mark.parametrize("case", ["trie", "unconstrained", "gumbel", "logits"])
+def test_bound_wait_fallback_keeps_result(lib, case):
+    """Beam workgroups of the fused pilot + per-beam kernel that stop waiting for their
+    request's bound at once (wait limit 0) admit every candidate; rows with more than top_k of
+    them go to the W-of-pool stage's overflow path.  The selection is unchanged: bit-exact
+    against the oracle on every step."""
+    rng = np.random.default_rng(21)
+    S = 3
+    if case == "trie":
+        wl = workload("tiny")
+        W, K, P = request_shapes(wl)
+        items = catalog_items(wl)
+        say("[select] wait limit 0: tiny trie")
+        select_loop_vs_oracle(lib, W, K, wl.C, wl.S, lambda d: logprob_rows(wl, d), items,
+                              label="wait0-trie", wait_limit=0)
+        return
+    W, K, C = [48, 64, 17], [48, 8, 17], 512
+    x = [rng.normal(0.0, 3.0, size=(sum(W), C)) for _ in range(S)]
+    lps = [np.minimum((v - np.log(np.exp(v).sum(axis=1, keepdims=True))).astype(np.float32), 0.0) for v in x]
+    say(f"[select] wait limit 0: {case}")
+    if case == "unconstrained":
+        select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wait0", wait_limit=0)
+    elif case == "gumbel":
+        g = [rng.gumbel(size=(sum(W), C)).astype(np.float32) for _ in range(S)]
+        select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wait0-gumbel", wait_limit=0,
+                              noise_of_step=lambda d: g[d], temperature=1.0)
+    else:
+        raw = [v.astype(np.float32) for v in x]
+        select_loop_vs_oracle(lib, W, K, C, S, lambda d: raw[d], None, label="wait0-logits", wait_limit=0,
+                              raw_logits=True)
