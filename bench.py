@@ -30,8 +30,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-DOMINANT = "attn_shared_lds_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_shared_lds_wide512_traffic.txt")
+DOMINANT = "attn_shared_split_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_shared_split_wide512_traffic.txt")
 KERNEL_SOURCES = ["generative_recommendation_wide_amd/csrc/attn_shared.hip",
                   "generative_recommendation_wide_amd/csrc/device_common.h",
                   "generative_recommendation_wide_amd/csrc/grw_internal.h"]

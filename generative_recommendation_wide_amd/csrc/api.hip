@@ -480,7 +480,7 @@ int attn_args(grw_ws* w, const void* q, const void* k_shared, const void* v_shar
 
 hipError_t launch_shared_stage(grw_ws* w, const AttnArgs& a, hipStream_t s) {
   if (!w->mfma) return launch_attn_shared_valu(a, w->d_work, w->n_work, s);
-  hipError_t e = launch_attn_shared_lds(a, w->d_work, w->n_wide, s);
+  hipError_t e = launch_attn_shared_split(a, w->d_work, w->n_wide, s);
   if (e == hipSuccess) e = launch_attn_shared_mfma(a, w->d_work + w->n_wide, w->n_work - w->n_wide, s);
   return e;
 }

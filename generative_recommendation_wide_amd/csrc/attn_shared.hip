@@ -348,24 +348,15 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
 }
 
 // ---------------------------------------------------------------------------------------
-// Wide-request bf16 path: 8 waves x 32 rows = 256 query rows per workgroup (one request's
-// 128 beams x 2 grouped heads), so each prompt tile read from L2 feeds twice the rows of the
-// 4-wave kernel above.  Tiles move global -> LDS with global_load_lds_dwordx4 (no register
-// staging, no LDS store instructions) into a two-stage ring.  Tiles are unpadded and
-// XOR-swizzled so the MFMA operand reads are conflict-free 16-byte reads:
+// Prompt tiles of the wide-request bf16 path.  Tiles move global -> LDS with
+// global_load_lds_dwordx4 (no register staging, no LDS store instructions).  They are
+// unpadded and XOR-swizzled so the MFMA operand reads are conflict-free 16-byte reads:
 //   K tile   [64 keys][128 d]: 16-byte chunk lc of row r sits at chunk lc ^ (r % 16);
 //            row r holds key k_row_key(r), a permutation inside each 32-key block chosen so
 //            that the eight P values a lane feeds one PV k-step are eight consecutive keys;
 //   V^T tile [128 d][64 keys]: chunk lc of row d sits at chunk lc ^ ((d / 2) % 8).
-// Each phase reads all its fragments before its MFMAs so one wait covers the LDS latency.
 // ---------------------------------------------------------------------------------------
 namespace lds {
-
-constexpr int NWAVES = 8;
-constexpr int NSTAGE = 2;
-constexpr int K_BYTES = NT * DH * 2;       // 16 KB
-constexpr int STAGE_BYTES = 2 * K_BYTES;   // K + V^T
-constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -375,33 +366,109 @@ __device__ __forceinline__ int k_row_key(int r) {
   return (r & 32) + (i >> 1) * 16 + hh * 8 + (i & 1) * 4 + j;
 }
 
-// Direct-to-LDS loads of the tile at prompt position p: each wave moves 2 KB of K and 2 KB
-// of V^T (lane l of an instruction fills LDS chunk base + l).
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* kb, const uint8_t* vb, int p, int Pp,
-                                           int wave, int lane) {
-  constexpr int PER = 16 / NWAVES;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int blk = wave * PER + i;
-    const int j = blk * 64 + lane;
-    {
-      const int r = j >> 4, lc = (j & 15) ^ (r & 15);
-      const uint8_t* src = kb + ((size_t)(p + k_row_key(r)) * DH + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + blk * 1024), 16, 0, 0);
-    }
-    {
-      const int d = j >> 3, lc = (j & 7) ^ ((d >> 1) & 7);
-      const uint8_t* src = vb + ((size_t)d * Pp + p + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + K_BYTES + blk * 1024), 16, 0, 0);
-    }
-  }
-}
-
 __device__ __forceinline__ void wait_all_vm() {
   __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | 0);   // vmcnt(0)
 }
 
-__global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_lds_kernel(AttnArgs a, const ShWork* __restrict__ work) {
+}  // namespace lds
+
+// ---------------------------------------------------------------------------------------
+// Wide-request bf16 path (W * g > 128 rows): 8 waves and 256 query rows (128 beams x 2
+// grouped heads) per workgroup, so each prompt tile read from L2 feeds twice the rows of
+// the 4-wave kernel above.  The roles are split: waves 0-3 (score waves) each compute
+// S^T = K Q^T and the softmax for 64 rows, and waves 4-7 (product waves) each accumulate
+// O^T += V^T P^T for the same 64 rows.  P goes from a score wave to its product wave through LDS (one 8 KB buffer per
+// wave pair and tile, in the MFMA B-operand layout, double buffered), with the per-row
+// rescale factor when the running max moves.  A score wave and its product wave share a
+// SIMD (wave w runs on SIMD w mod 4), so the product wave's MFMAs can run while the score
+// wave does its exponentials, and each K or V fragment read from LDS feeds two MFMAs (two
+// 32-row blocks) instead of one.  Iteration i: score waves handle tile i, product waves
+// tile i - 1; one barrier per iteration.
+// ---------------------------------------------------------------------------------------
+namespace split {
+
+constexpr int NWAVES = 8;
+constexpr int TILE_BYTES = NT * DH * 2;               // 16 KB: one K or V^T tile
+constexpr int KRING = 0;                              // K tiles [2]
+constexpr int VRING = 2 * TILE_BYTES;                 // V^T tiles [2]
+constexpr int P_WAVE = 2 * 4 * 64 * 16;               // P of one score wave: [2 qb][4 ks][64 lanes][16 B]
+constexpr int PBUF = 4 * TILE_BYTES;                  // P [2 buffers][4 score waves]
+constexpr int ALPHA = PBUF + 2 * 4 * P_WAVE;          // rescale factors [2][4][64] float
+constexpr int FLAG = ALPHA + 2 * 4 * 64 * 4;          // rescale flags [2][4] int
+constexpr int SMEM_BYTES = FLAG + 2 * 4 * 4;
+
+// Direct-to-LDS loads of one K tile (rows in k_row_key order, swizzled) and one V^T tile:
+// each wave moves 2 KB of each.
+__device__ __forceinline__ void issue_k(uint8_t* dst, const uint8_t* kb, int p, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = wave * 2 + i;
+    const int j = blk * 64 + lane;
+    const int r = j >> 4, lc = (j & 15) ^ (r & 15);
+    const uint8_t* src = kb + ((size_t)(p + lds::k_row_key(r)) * DH + lc * 8) * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds::lds_void*)(dst + blk * 1024), 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void issue_v(uint8_t* dst, const uint8_t* vb, int p, int Pp, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = wave * 2 + i;
+    const int j = blk * 64 + lane;
+    const int d = j >> 3, lc = (j & 7) ^ ((d >> 1) & 7);
+    const uint8_t* src = vb + ((size_t)d * Pp + p + lc * 8) * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds::lds_void*)(dst + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Normalised partial output and LSE of one 32-row block (rows row0 .. row0 + 31 of the
+// request's W*g rows, lane l32 holding row row0 + l32 in o), written as whole 512-byte
+// rows through the 8 KB LDS buffer tb (16-byte chunk c of row r at c ^ (r % 16)).
+__device__ __forceinline__ void store_rows(const AttnArgs& a, const ShWork& wk, const ReqDesc& rd, uint8_t* tb,
+                                           const floatx16 (&o)[DH / 32], float m, float l, int row0) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int g = a.g, Hq = a.Hq, h = wk.h;
+  const int nrows = rd.W * g;
+  const int mrow = row0 + l32;
+  const bool row_ok = mrow < nrows;
+  const float inv = row_ok ? 1.0f / l : 0.0f;
+  if (row_ok && hi == 0) {
+    const int b = mrow / g;
+    a.lpart[((size_t)wk.split * a.sumW + rd.boff + b) * Hq + h * g + (mrow - b * g)] = (m + fast_log2(l)) * kLn2;
+  }
+  const int rrow = lane >> 4, rch = lane & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int db2 = 0; db2 < 2; ++db2) {
+      const int db = half * 2 + db2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = db2 * 8 + i * 2 + hi;
+        const floatx4 v = {o[db][i * 4 + 0] * inv, o[db][i * 4 + 1] * inv, o[db][i * 4 + 2] * inv,
+                           o[db][i * 4 + 3] * inv};
+        *(floatx4*)(tb + l32 * 256 + ((ch ^ (l32 & 15)) << 4)) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + rrow;
+      const floatx4 v = *(const floatx4*)(tb + r * 256 + ((rch ^ (r & 15)) << 4));
+      const int mr = row0 + r;
+      if (mr < nrows) {
+        const int bb = mr / g;
+        const int qq = h * g + (mr - bb * g);
+        float* dst = a.opart + (((size_t)wk.split * a.sumW + rd.boff + bb) * Hq + qq) * DH;
+        *(floatx4*)(dst + half * 64 + rch * 4) = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnArgs a, const ShWork* __restrict__ work) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const ShWork wk = work[blockIdx.x];
   if (wk.r < 0) return;
@@ -410,127 +477,203 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_lds_kernel(AttnArg
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = a.g, Hq = a.Hq, h = wk.h;
   const int nrows = rd.W * g;
-  const int mrow = wk.m0 + wave * 32 + l32;
-  const bool row_ok = mrow < nrows;
-  const int b = row_ok ? mrow / g : 0;
-  const int qh = h * g + (row_ok ? mrow - b * g : 0);
-  const int slot = rd.boff + b;
+  const bool scorer = wave < 4;
+  const int sw = wave & 3;                  // the pair: rows wk.m0 + sw * 64 .. + 63
   const uint8_t* kb = (const uint8_t*)a.k_shared + (rd.kv_off + (size_t)h * rd.Pp * DH) * 2;
   const uint8_t* vb = (const uint8_t*)a.v_shared + (rd.kv_off + (size_t)h * DH * rd.Pp) * 2;
   const int p0 = wk.p0, p1 = wk.p1;
   const int ntiles = (p1 - p0 + NT - 1) / NT;
+  float* const alpha_s = (float*)(smem + ALPHA);
+  int* const flag_s = (int*)(smem + FLAG);
 
-  issue_tile(smem, kb, vb, p0, rd.Pp, wave, lane);
-  bf16x8 qf[DH / 16];
-  {
-    const __bf16* qrow = (const __bf16*)a.q + ((size_t)slot * Hq + qh) * DH;
+  issue_k(smem + KRING, kb, p0, wave, lane);
+
+  if (scorer) {
+    // ---------------- score wave: S^T, running max, P ----------------
+    const float c = rsqrtf((float)DH) * kLog2e;
+    bf16x8 qf[2][DH / 16];
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
-      if (row_ok) {
-        qf[ks] = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
-      } else {
+    for (int qb = 0; qb < 2; ++qb) {
+      const int mrow = wk.m0 + sw * 64 + qb * 32 + l32;
+      const bool ok = mrow < nrows;
+      const int b = ok ? mrow / g : 0;
+      const int qh = h * g + (ok ? mrow - b * g : 0);
+      const __bf16* qrow = (const __bf16*)a.q + ((size_t)(rd.boff + b) * Hq + qh) * DH;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.0f;
+      for (int ks = 0; ks < DH / 16; ++ks) {
+        if (ok) {
+          qf[qb][ks] = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (__bf16)0.0f;
+        }
       }
     }
-  }
-  const float c = rsqrtf((float)DH) * kLog2e;
-  float m_run = -INFINITY, l_run = 0.0f;
-  floatx16 o[DH / 32];
+    float m_run[2] = {-INFINITY, -INFINITY};
+    for (int i = 0; i <= ntiles; ++i) {
+      lds::wait_all_vm();
+      __syncthreads();
+      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, lane);
+      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, rd.Pp, wave, lane);
+      if (i == ntiles) break;
+      const uint8_t* st = smem + KRING + (i & 1) * TILE_BYTES;
+      const int p = p0 + i * NT;
+      floatx16 s[2][2];   // [key block][row block]
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db) o[db] = floatx16{};
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  for (int t = 0; t < ntiles; ++t) {
-    wait_all_vm();            // this wave's loads of tile t are in LDS
-    __syncthreads();          // ... and every other wave's; the other stage is free again
-    if (t + 1 < ntiles) issue_tile(smem + ((t + 1) & 1) * STAGE_BYTES, kb, vb, p0 + (t + 1) * NT, rd.Pp, wave, lane);
-    const uint8_t* st = smem + (t & 1) * STAGE_BYTES;
-    const int p = p0 + t * NT;
-
-    floatx16 s0 = floatx16{}, s1 = floatx16{};
-    {
-      bf16x8 kf[2][DH / 16];
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        const int lc = 2 * ks + hi;
-        kf[0][ks] = *(const bf16x8*)(st + l32 * 256 + ((lc ^ (l32 & 15)) << 4));
-        kf[1][ks] = *(const bf16x8*)(st + (32 + l32) * 256 + ((lc ^ (l32 & 15)) << 4));
+        for (int qb = 0; qb < 2; ++qb) s[kb2][qb] = floatx16{};
+      __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 kf[2][4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int lc = 2 * (h2 * 4 + k4) + hi;
+          kf[0][k4] = *(const bf16x8*)(st + l32 * 256 + ((lc ^ (l32 & 15)) << 4));
+          kf[1][k4] = *(const bf16x8*)(st + (32 + l32) * 256 + ((lc ^ (l32 & 15)) << 4));
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              s[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb2][k4], qf[qb][h2 * 4 + k4], s[kb2][qb], 0, 0, 0);
       }
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int ks = 0; ks < DH / 16; ++ks) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][ks], qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1][ks], qf[ks], s1, 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // all K fragment reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 score MFMAs
       __builtin_amdgcn_s_setprio(0);
-    }
-    // value k of block kb is key p + kb*32 + (k/8)*16 + hi*8 + ((k/4)%2)*4 + k%4
-    if (p + NT > p1) {
+      // value k of key block kb2 is key p + kb2*32 + (k/8)*16 + hi*8 + ((k/4)%2)*4 + k%4
+      if (p + NT > p1) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int key = p + ((k >> 3) << 4) + hi * 8 + (((k >> 2) & 1) << 2) + (k & 3);
-        if (key >= p1) s0[k] = -INFINITY;
-        if (key + 32 >= p1) s1[k] = -INFINITY;
+        for (int k = 0; k < 16; ++k) {
+          const int key = p + ((k >> 3) << 4) + hi * 8 + (((k >> 2) & 1) << 2) + (k & 3);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            if (key >= p1) s[0][qb][k] = -INFINITY;
+            if (key + 32 >= p1) s[1][qb][k] = -INFINITY;
+          }
+        }
+      }
+      float mx[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(s[0][qb][k], s[1][qb][k]));
+        mx[qb] = fmaxf(m, __shfl_xor(m, 32, 64)) * c;
+      }
+      // lazy rescale as in the kernels above; the product wave applies the factor to O and l
+      const int bi = (i & 1) * 4 + sw;
+      const bool resc = __any(mx[0] > m_run[0] + kRescale || mx[1] > m_run[1] + kRescale);
+      if (resc) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mx[qb]);
+          const float al = fast_exp2(m_run[qb] - m_new);   // m_run = -inf -> 0
+          m_run[qb] = m_new;
+          if (hi == 0) alpha_s[bi * 64 + qb * 32 + l32] = al;
+        }
+      }
+      if (lane == 0) flag_s[bi] = resc ? 1 : 0;
+      uint8_t* pw = smem + PBUF + bi * P_WAVE;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            float e[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) e[x] = fast_exp2(fmaf(s[kb2][qb][half * 8 + x], c, -m_run[qb]));
+            const int ks = kb2 * 2 + half;
+            *(bf16x8*)(pw + ((qb * 4 + ks) * 64 + lane) * 16) = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          }
+        }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s0[k], s1[k]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    if (__any(mx > m_run + kRescale)) {   // lazy rescale (see the 4-wave kernel)
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db) o[db] *= alpha;
-      m_run = m_new;
+    __syncthreads();   // every product wave is past its last tile
+    if (hi == 0) {
+      alpha_s[sw * 64 + l32] = m_run[0];
+      alpha_s[sw * 64 + 32 + l32] = m_run[1];
     }
-    // V^T fragments of all four k-steps, read before the exponentials so their latency hides
-    const uint8_t* vt = st + K_BYTES;
-    bf16x8 vf[4][DH / 32];
+    __syncthreads();
+  } else {
+    // ---------------- product wave: O^T += V^T P^T, row sums ----------------
+    floatx16 o[2][DH / 32];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int lc = 2 * ks + hi;
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
-        const int d = db * 32 + l32;
-        vf[ks][db] = *(const bf16x8*)(vt + d * 128 + ((lc ^ ((d >> 1) & 7)) << 4));
+      for (int db = 0; db < DH / 32; ++db) o[qb][db] = floatx16{};
+    float l_run[2] = {0.0f, 0.0f};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    for (int i = 0; i <= ntiles; ++i) {
+      lds::wait_all_vm();
+      __syncthreads();
+      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, lane);
+      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, rd.Pp, wave, lane);
+      if (i == 0) continue;
+      const int bt = ((i - 1) & 1) * 4 + sw;
+      if (flag_s[bt]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float al = alpha_s[bt * 64 + qb * 32 + l32];
+          l_run[qb] *= al;
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db) o[qb][db] *= al;
+        }
       }
+      const uint8_t* pp = smem + PBUF + bt * P_WAVE;
+      const uint8_t* vt = smem + VRING + ((i - 1) & 1) * TILE_BYTES;
+      bf16x8 pf[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) pf[qb][ks] = *(const bf16x8*)(pp + ((qb * 4 + ks) * 64 + lane) * 16);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 vf[2][DH / 32];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int lc = 2 * (h2 * 2 + k2) + hi;
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db) {
+            const int d = db * 32 + l32;
+            vf[k2][db] = *(const bf16x8*)(vt + d * 128 + ((lc ^ ((d >> 1) & 7)) << 4));
+          }
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k2][db], pf[qb][h2 * 2 + k2], o[qb][db], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      // row sums of the bf16 P the products used
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qb][ks], pf[qb][ks], 0, 1), ones, l_run[qb], false);
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qb][ks], pf[qb][ks], 2, 3), ones, l_run[qb], false);
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qb][ks], pf[qb][ks], 4, 5), ones, l_run[qb], false);
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[qb][ks], pf[qb][ks], 6, 7), ones, l_run[qb], false);
+        }
     }
+    __syncthreads();   // every wave is past its last tile: the rings are free
+    __syncthreads();   // the score waves' final running maxima are in alpha_s
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      s0[k] = fast_exp2(fmaf(s0[k], c, -m_run));
-      s1[k] = fast_exp2(fmaf(s1[k], c, -m_run));
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m = alpha_s[sw * 64 + qb * 32 + l32];
+      const float l = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+      store_rows(a, wk, rd, smem + KRING + sw * TILE_BYTES, o[qb], m, l, wk.m0 + sw * 64 + qb * 32);
     }
-    bf16x8 pb[4];
-    pb[0] = pack_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
-    pb[1] = pack_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
-    pb[2] = pack_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
-    pb[3] = pack_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 0, 1), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 2, 3), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 4, 5), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 6, 7), ones, l_run, false);
-    }
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][db], pb[ks], o[db], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
   }
-
-  __syncthreads();   // every wave is past its last tile: the ring is free
-  store_partial(a, wk, rd, smem, o, m_run, l_run, row_ok, slot, qh, 1.0f);
 }
 
-}  // namespace lds
+}  // namespace split
 
 
 // ---------------------------------------------------------------------------------------
@@ -616,16 +759,16 @@ hipError_t launch_attn_shared_mfma(const AttnArgs& a, const ShWork* work, int n_
   return hipGetLastError();
 }
 
-hipError_t launch_attn_shared_lds(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s) {
+hipError_t launch_attn_shared_split(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
-  static bool attr_set = false;   // the ring needs more than the default 64 KB of LDS
+  static bool attr_set = false;   // the rings and P buffers need more than the default 64 KB of LDS
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lds::attn_shared_lds_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds::SMEM_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)split::attn_shared_split_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, split::SMEM_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  lds::attn_shared_lds_kernel<<<n_work, lds::NWAVES * 64, lds::SMEM_BYTES, s>>>(a, work);
+  split::attn_shared_split_kernel<<<n_work, split::NWAVES * 64, split::SMEM_BYTES, s>>>(a, work);
   return hipGetLastError();
 }
 

@@ -120,7 +120,7 @@ hipError_t launch_attn_shared_mfma(const AttnArgs& a, const ShWork* work, int n_
                                    hipStream_t s);
 hipError_t launch_attn_shared_valu(const AttnArgs& a, const ShWork* work, int n_work,
                                    hipStream_t s);
-hipError_t launch_attn_shared_lds(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s);
+hipError_t launch_attn_shared_split(const AttnArgs& a, const ShWork* work, int n_work, hipStream_t s);
 hipError_t launch_attn_unshared(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_unshared_merge(const AttnArgs& a, hipStream_t s);
