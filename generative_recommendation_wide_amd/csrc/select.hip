@@ -942,7 +942,10 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
 // Output slot `rank` of the request: token, parent, exact score, trie child.
 // edge: the CSR edge of the entry when the per-beam stage recorded it (its child is node
 // edge + 1), else -1 (the child is then found by a binary search of the parent's row).
-template <bool X>
+// Without noise the entry's key is its score, fl32(score + lp), so the score is read from
+// the composite; a zero key is recomputed from its operands, since the ordered key does not
+// tell -0.0 from +0.0.  With noise (G) the key holds the noise and the score is recomputed.
+template <bool G, bool X>
 __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int rank, uint64_t v, int edge = -1) {
   const int C = a.C;
   const int slot = rd.boff + rank;
@@ -958,8 +961,11 @@ __device__ __forceinline__ void emit(const SelArgs& a, const ReqDesc& rd, int ra
     return;
   }
   const int ps = rd.boff + (int)b;
-  const float x = a.logprobs[(size_t)ps * C + c];
-  const float score = a.scores[ps] + (X ? x - a.row_lse[ps] : x);
+  float score = G ? 0.0f : float_of_ordered((uint32_t)(v >> 32));
+  if (G || score == 0.0f) {
+    const float x = a.logprobs[(size_t)ps * C + c];
+    score = a.scores[ps] + (X ? x - a.row_lse[ps] : x);
+  }
   int node = -1;
   if (a.row_ptr != nullptr && edge >= 0) {
     node = edge + 1;
@@ -1201,7 +1207,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
       const int s0 = (int)L.start[b], e0 = (int)L.start[b + 1];
       int rank = s0;
       for (int q = s0; q < e0; ++q) rank += L.win[q] > v;
-      if (rank < nsel) emit<X>(a, rd, rank, v, EDGES ? L.wedge[p] : -1);
+      if (rank < nsel) emit<G, X>(a, rd, rank, v, EDGES ? L.wedge[p] : -1);
     }
   } else if (nsel > 0) {
     // fallback: radix select of the W-th entry, gather, bitonic sort
@@ -1240,7 +1246,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
         __syncthreads();
       }
     }
-    for (int i = tid; i < nsel; i += NT) emit<X>(a, rd, i, L.win[i]);
+    for (int i = tid; i < nsel; i += NT) emit<G, X>(a, rd, i, L.win[i]);
   }
   for (int i = nsel + tid; i < W; i += NT) {
     const int slot = rd.boff + i;
