@@ -55,6 +55,9 @@ struct grw_ws {
   int n_wide = 0;                // leading items of the work list that use the 8-wave kernel
   int n_pilots = 0;              // pilot workgroups of the deterministic selection
   int n_pilots_s = 0;            // pilot workgroups of the sampled selection
+  int n_pilots_w = 0;            // ... of the general kernels, deterministic
+  int n_pilots_ws = 0;           // ... of the general kernels, sampled
+  int pilot_cap = 0;             // pilot-buffer entries per request
   int32_t wait_limit = kBoundSpin;   // polls of a beam workgroup waiting for its bound
   std::vector<ReqDesc> req;
 };
@@ -176,20 +179,26 @@ void build_mfma_work(grw_ws* w, std::vector<ShWork>& out, int& n_wide) {
 // candidates, and at most 64 for the sampled one: there noise decides the slot order, and
 // contributions spread over more beams bound the W-th best key far more tightly (kept pool
 // 24 K -> 6.8 K entries on the W = K = 512 workload at temperature 1).
-int pilot_count(const ReqDesc& d, int max_per, int& per) {
+int pilot_count(const ReqDesc& d, int max_per, int& per, int max_pilots = kMaxPilots, int cap = kPilotCap) {
   per = 1;
   while (per * 2 <= std::min(d.K, max_per)) per *= 2;
   const int64_t want = ceil_div(8LL * d.W, per);
-  const int J = (int)std::min<int64_t>({(int64_t)d.W, (int64_t)kMaxPilots, (int64_t)(kPilotCap / per), want});
+  const int J = (int)std::min<int64_t>({(int64_t)d.W, (int64_t)max_pilots, (int64_t)(cap / per), want});
   return std::max(1, J);
 }
 
-void set_pilots(ReqDesc& d, int32_t& pilot_off) {
+// The general kernels (rows longer than 8192 codes, or W > 1024) take up to kMaxPilotsWide
+// pilots and kPilotCapWide candidates, so that requests wider than kPilotCap still get a
+// bound (at top_k = 64, W up to about 16000).
+void set_pilots(ReqDesc& d, int32_t& pilot_off, int cap) {
   int per;
   d.n_pilot = pilot_count(d, 256, per);
   d.n_pilot_s = pilot_count(d, 64, per);
+  const bool wide = cap >= kPilotCapWide;
+  d.n_pilot_w = wide ? pilot_count(d, 256, per, kMaxPilotsWide, kPilotCapWide) : d.n_pilot;
+  d.n_pilot_ws = wide ? pilot_count(d, 64, per, kMaxPilotsWide, kPilotCapWide) : d.n_pilot_s;
   d.pilot_off = pilot_off;
-  pilot_off += kPilotCap;
+  pilot_off += cap;
 }
 
 // Work list of the generic VALU shared stage: one item per (slot, query head, split).
@@ -275,15 +284,17 @@ int grw_ws_create(const grw_limits* limits, grw_ws** out) {
   if (st == GRW_OK) st = dev_alloc(&w->d_pool_edge, w->pool_cap);
   if (st == GRW_OK) st = dev_alloc(&w->d_surv_count, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_bound, L.max_requests);
-  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 8 * B);
+  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_desc, 16 * B);
   if (st == GRW_OK) st = dev_alloc(&w->d_row_lse, B);
   if (st == GRW_OK) st = dev_alloc(&w->d_step_state, (int64_t)L.max_requests);
   if (st == GRW_OK) st = dev_alloc(&w->d_sync, (int64_t)L.max_requests * kSyncCopies * kSyncStride);
-  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * kPilotCap);
+  // the general kernels run when rows can be longer than 8192 codes or W larger than 1024
+  w->pilot_cap = (L.max_C > kOnePass || L.max_W > 1024) ? kPilotCapWide : kPilotCap;
+  if (st == GRW_OK) st = dev_alloc(&w->d_pilot_buf, (int64_t)L.max_requests * w->pilot_cap);
   if (st == GRW_OK) st = dev_alloc(&w->d_flags, 1);
   if (st == GRW_OK) {
     w->stage_bytes = sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * B + sizeof(ShWork) * items +
-                     sizeof(int32_t) * 8 * B;
+                     sizeof(int32_t) * 16 * B;
     if (hipHostMalloc(&w->h_stage, w->stage_bytes, hipHostMallocDefault) != hipSuccess) {
       w->h_stage = nullptr;
       st = GRW_ENOMEM;
@@ -337,7 +348,7 @@ int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32
     d.nsplit = 1;
     d.kv_off = kv * L.Hkv * L.D;
     d.pool_off = pool;
-    set_pilots(d, pilot_off);
+    set_pilots(d, pilot_off, w->pilot_cap);
     sumW += W;
     kv += d.Pp;
     pool += (int64_t)W * K;
@@ -364,17 +375,21 @@ int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32
   ShWork* hwork = (ShWork*)(h + sizeof(ReqDesc) * L.max_requests + sizeof(int32_t) * L.max_total_beams);
   int32_t* hpilot = (int32_t*)(hwork + w->work_cap);
   std::memcpy(hreq, w->req.data(), sizeof(ReqDesc) * n_requests);
-  // pilot descriptors {slot, request, first pilot-buffer entry, threads per group}: the
-  // deterministic selection's, then the sampled selection's
-  int n_pilots = 0, n_pilots_s = 0;
+  // pilot descriptors {slot, request, first pilot-buffer entry, threads per group}, four
+  // sets: the register-resident path's deterministic and sampled selections, then the
+  // general kernels' deterministic and sampled selections
+  int np[4] = {0, 0, 0, 0};
   for (int r = 0; r < n_requests; ++r)
     for (int b = 0; b < req[r].W; ++b) hslot[req[r].boff + b] = r;
-  for (int v = 0; v < 2; ++v) {
-    int32_t* hp = hpilot + (v == 0 ? 0 : 4 * n_pilots);
+  const bool wide = w->pilot_cap >= kPilotCapWide;
+  int32_t* hp = hpilot;
+  for (int v = 0; v < 4; ++v) {
     int n = 0;
     for (int r = 0; r < n_requests; ++r) {
       int per;
-      const int J = pilot_count(req[r], v == 0 ? 256 : 64, per);
+      const int max_per = (v & 1) ? 64 : 256;
+      const int J = (v >= 2 && wide) ? pilot_count(req[r], max_per, per, kMaxPilotsWide, kPilotCapWide)
+                                     : pilot_count(req[r], max_per, per);
       for (int j = 0; j < J; ++j, ++n) {
         hp[4 * n + 0] = req[r].boff + j;
         hp[4 * n + 1] = r;
@@ -382,8 +397,10 @@ int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32
         hp[4 * n + 3] = 256 / per;
       }
     }
-    (v == 0 ? n_pilots : n_pilots_s) = n;
+    np[v] = n;
+    hp += 4 * n;
   }
+  const int n_pilots = np[0], n_pilots_s = np[1];
   std::memcpy(hwork, work.data(), sizeof(ShWork) * work.size());
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(w->d_req, hreq, sizeof(ReqDesc) * n_requests, hipMemcpyHostToDevice, s);
@@ -391,7 +408,7 @@ int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32
   if (e == hipSuccess && !work.empty())
     e = hipMemcpyAsync(w->d_work, hwork, sizeof(ShWork) * work.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(w->d_pilot_desc, hpilot, sizeof(int32_t) * 4 * (n_pilots + n_pilots_s),
+    e = hipMemcpyAsync(w->d_pilot_desc, hpilot, sizeof(int32_t) * 4 * (np[0] + np[1] + np[2] + np[3]),
                        hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
@@ -402,6 +419,8 @@ int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32
   w->n_wide = n_wide;
   w->n_pilots = n_pilots;
   w->n_pilots_s = n_pilots_s;
+  w->n_pilots_w = np[2];
+  w->n_pilots_ws = np[3];
   w->maxW = maxW;
   w->maxK = maxK;
   w->bound = true;
@@ -580,8 +599,13 @@ int select_step(grw_ws* w, const float* logprobs, bool raw_logits, const float* 
   a.surv_count = w->d_surv_count;
   a.pool_edge = w->d_pool_edge;
   a.bound = w->d_bound;
-  a.pilot_desc = w->d_pilot_desc + (noise != nullptr ? 4 * w->n_pilots : 0);
-  a.n_pilots = noise != nullptr ? w->n_pilots_s : w->n_pilots;
+  if (select_fused_ok(C, w->maxW)) {
+    a.pilot_desc = w->d_pilot_desc + (noise != nullptr ? 4 * w->n_pilots : 0);
+    a.n_pilots = noise != nullptr ? w->n_pilots_s : w->n_pilots;
+  } else {
+    a.pilot_desc = w->d_pilot_desc + 4 * (w->n_pilots + w->n_pilots_s) + (noise != nullptr ? 4 * w->n_pilots_w : 0);
+    a.n_pilots = noise != nullptr ? w->n_pilots_ws : w->n_pilots_w;
+  }
   a.pilot_buf = w->d_pilot_buf;
   a.pilot_count = w->d_step_state;
   a.sync = w->d_sync;

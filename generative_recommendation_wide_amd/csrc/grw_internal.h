@@ -19,6 +19,8 @@ struct ReqDesc {
   int32_t n_pilot;   // pilot beams of the selection (slots boff .. boff + n_pilot - 1)
   int32_t n_pilot_s; // pilot beams of the sampled (Gumbel) selection
   int32_t pilot_off; // first pilot-buffer entry of the request
+  int32_t n_pilot_w;   // pilot beams of the general kernels (rows longer than 8192 codes or
+  int32_t n_pilot_ws;  //   W > 1024), deterministic and sampled: up to kPilotCapWide entries
   int32_t pad_;
 };
 
@@ -46,6 +48,8 @@ constexpr int kRegC = 32;          // candidates per thread of the one-pass per-
 constexpr int kOnePass = 256 * kRegC;   // rows up to this length take the one-pass path
 constexpr int kMaxPilots = 64;     // pilot beams per request
 constexpr int kPilotCap = 4096;    // pilot candidates per request
+constexpr int kMaxPilotsWide = 1024;    // pilot beams per request on the general kernels
+constexpr int kPilotCapWide = 16384;    // pilot candidates per request on the general kernels
 constexpr int kSyncCopies = 32;    // copies of a request's step-state word (spread polling)
 constexpr int kSyncStride = 32;    // words between copies (256 bytes)
 constexpr int kBoundSpin = 1 << 18;   // default polls of a beam workgroup waiting for its bound
@@ -101,7 +105,7 @@ struct SelArgs {
   const int32_t* pilot_desc;   // [n_pilots][4] beam slot, request, first pilot-buffer entry,
                                // threads per group, of each pilot workgroup
   int32_t n_pilots;
-  uint64_t* pilot_buf;      // [R][kPilotCap] pilot candidates
+  uint64_t* pilot_buf;      // [R][pilot capacity] pilot candidates
   uint32_t* pilot_count;    // [R] pilots finished this step
   int32_t wait_limit;       // polls before a waiting beam workgroup proceeds without the bound
   uint64_t* sync;           // [R][kSyncCopies] words kSyncStride apart: the request's step

@@ -605,6 +605,15 @@ __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
 // wait until this thread's stores are acknowledged at device scope
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier that publishes LDS operations but leaves global loads in flight
+// (__syncthreads also waits for every outstanding load, which would cancel a prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Step-state word: bit 63 set once the request's bound (low 32 bits) is published.
 constexpr uint64_t kSyncBound = 1ull << 63;
 
@@ -642,8 +651,9 @@ struct PilotLds {
 // Pilot workgroup `pi`.  PUBLISH (pilots inside the per-beam kernel): the request's last
 // pilot stores the bound with a device-coherent store and, once that store is acknowledged,
 // sets the request's ready word that the kernel's beam workgroups wait on.
-// LT >= 0: every row of the launch has that layout and fits the one-read path.
-template <bool G, bool X, bool PUBLISH, int LT = -1>
+// LT >= 0: every row of the launch has that layout and fits the one-read path.  WIDE: the
+// general kernels' pilot set (up to kPilotCapWide contributions per request).
+template <bool G, bool X, bool PUBLISH, int LT = -1, bool WIDE = false>
 __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S) {
   uint64_t* red64 = S.red64;
   float* redf = S.redf;
@@ -682,13 +692,38 @@ __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S)
         best = row_best<kFullScalar, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd);
       else best = row_best<kTrie, G, X>(a, slot, lprow, grow, codes, cnt, s, flat_base, fl, redf, redd, mask);
     } else {
-      const float lse = X ? a.row_lse[slot] : 0.0f;    // long rows: computed by select_lse_kernel
-      for (int q = tid; q < cnt; q += 256) {
-        const int c = codes ? codes[q] : q;
-        if ((unsigned)c >= (unsigned)a.C) continue;
-        const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
-        const float lp = X ? lprow[c] - lse : lprow[c];
-        best = max(best, candidate<G>(s, lp, tg, flat_base + (uint32_t)c, fl));
+      // long rows (lse computed by select_lse_kernel): 16 positions per thread per round,
+      // their loads issued together
+      const float lse = X ? a.row_lse[slot] : 0.0f;
+      for (int q0 = 0; q0 < cnt; q0 += 256 * 16) {
+        int cc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int q = q0 + tid + 256 * u;
+          cc[u] = q < cnt ? (codes ? codes[q] : q) : -1;
+          if ((unsigned)cc[u] >= (unsigned)a.C) cc[u] = -1;
+        }
+        float lp[16], tg[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          lp[u] = cc[u] >= 0 ? (X ? lprow[cc[u]] - lse : lprow[cc[u]]) : -INFINITY;
+          tg[u] = (G && cc[u] >= 0) ? noise_term(a, grow, cc[u], fl) : 0.0f;
+        }
+        // the best key of the round in the float domain, then the composite of its first
+        // (lowest-code) position: the same maximum as over the composites
+        float mk = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float k = cc[u] >= 0 ? order_key<G>(s + lp[u], tg[u]) : -INFINITY;
+          mk = k > mk ? k : mk;          // NaN keys never win
+        }
+        if (mk != -INFINITY) {
+          int uf = 0;
+#pragma unroll
+          for (int u = 15; u >= 0; --u)
+            if (cc[u] >= 0 && order_key<G>(s + lp[u], tg[u]) == mk) uf = u;
+          best = max(best, candidate<G>(s, lp[uf], tg[uf], flat_base + (uint32_t)cc[uf], fl));
+        }
       }
     }
   }
@@ -705,12 +740,12 @@ __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S)
   if (tid % gsz == 0) st_dev(&a.pilot_buf[pd.z + tid / gsz], best);
   wait_stores();
   __syncthreads();
-  const int n_pilot = G ? rd.n_pilot_s : rd.n_pilot;
+  const int n_pilot = WIDE ? (G ? rd.n_pilot_ws : rd.n_pilot_w) : (G ? rd.n_pilot_s : rd.n_pilot);
   if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(n_pilot - 1);
   __syncthreads();
   if (!last_s) return;
   // the W_r-th best key of all contributions bounds the request's W_r-th best pool entry
-  constexpr int NP = kPilotCap / 256;
+  constexpr int NP = (WIDE ? kPilotCapWide : kPilotCap) / 256;
   const int n_ent = n_pilot * (256 / gsz);
   const uint64_t* pb = a.pilot_buf + rd.pilot_off;
   uint32_t pk[NP];
@@ -742,10 +777,12 @@ __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S)
   }
 }
 
+// The general kernels' pilots (the register-resident path runs its pilots inside
+// select_pilot_beam_kernel).
 template <bool G, bool X>
 __global__ __launch_bounds__(256) void select_pilot_kernel(SelArgs a) {
   __shared__ PilotLds S;
-  pilot_run<G, X, false>(a, blockIdx.x, S);
+  pilot_run<G, X, false, -1, true>(a, blockIdx.x, S);
 }
 
 // --------------------------------------------------------------------------------------
@@ -872,35 +909,74 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
     // ---- long rows: stream through the LDS buffer ----
     if (tid == 0) cnt_s = 0;
     __syncthreads();
+    // rounds of kLongChunk candidates (8 per thread, their loads issued together, and the
+    // next round's issued before this round is filtered); the buffer is trimmed to top K
+    // (<= kSelCap - kLongChunk) before a round could overflow it
+    constexpr int kLongChunk = 2048;
+    static_assert(kMaxK + kLongChunk <= kSelCap, "a trimmed buffer must take a whole round");
+    const float lse = X ? a.row_lse[slot] : 0.0f;
+    auto load_round = [&](int base, int (&cc)[8], float (&lp)[8], float (&tg)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = base + tid + 256 * k;
+        cc[k] = i < cnt ? (codes ? codes[i] : i) : -1;
+        if (i < cnt && (unsigned)cc[k] >= (unsigned)a.C) {   // corrupt trie row: never read outside it
+          fl |= GRW_FLAG_BAD_NODE;
+          cc[k] = -1;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        lp[k] = cc[k] >= 0 ? (X ? lprow[cc[k]] - lse : lprow[cc[k]]) : -INFINITY;
+        tg[k] = (G && cc[k] >= 0) ? noise_term(a, grow, cc[k], fl) : 0.0f;
+      }
+    };
+    // one round: trim if needed, filter the loaded candidates, append the survivors (reached
+    // by every thread; two register sets alternate so that no loaded register is copied)
     int n = 0;
-    for (int base = 0; base < cnt; base += kSelChunk) {
-      if (n + kSelChunk > kSelCap) {             // buffer full: keep the top K, raise tau
+    auto run_round = [&](const int (&cc)[8], const float (&lp)[8], const float (&tg)[8]) __attribute__((always_inline)) {
+      if (n + kLongChunk > kSelCap) {            // buffer full: keep the top K, raise tau
         const uint64_t T = block_select_threshold<256>([&](int i) { return buf[i]; }, n, K, hist, scr);
         n = block_compact_ge(buf, n, T, &cnt_s);
         const uint32_t tk = (uint32_t)(T >> 32);
         tau = max(tau, tk);
         tau = max(tau, __hip_atomic_load(&a.bound[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       }
-      uint64_t e[4];
+      // admission in the float domain (key >= tau_f exactly when its ordered key >= tau, for
+      // non-NaN keys); composites only for the admitted
+      const float tau_f = tau < 0x00800000u ? -3.402823466e+38f : float_of_ordered(tau);
+      uint64_t e[8];
       int ne = 0;
+      bool suspect = false;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = base + tid + 256 * k;
-        if (i < cnt) {
-          const int c = codes ? codes[i] : i;
-          if ((unsigned)c >= (unsigned)a.C) {      // corrupt trie row: never read outside the row
-            fl |= GRW_FLAG_BAD_NODE;
-            continue;
-          }
-          const float tg = G ? noise_term(a, grow, c, fl) : 0.0f;
-          const float lp = X ? lprow[c] - a.row_lse[slot] : lprow[c];
-          const uint64_t x = candidate<G>(s, lp, tg, flat_base + (uint32_t)c, fl);
+      for (int k = 0; k < 8; ++k) {
+        suspect |= cc[k] >= 0 && !(lp[k] <= 0.0f);
+        if (cc[k] >= 0 && order_key<G>(s + lp[k], tg[k]) >= tau_f) {
+          const uint64_t x = candidate<G>(s, lp[k], tg[k], flat_base + (uint32_t)cc[k], fl);
           if (x != 0 && (uint32_t)(x >> 32) >= tau) e[ne++] = x;
         }
       }
-      block_append<4>(buf, &cnt_s, e, ne);
-      __syncthreads();
+      if (suspect) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (cc[k] < 0) continue;
+          if (__builtin_isnan(lp[k])) fl |= GRW_FLAG_NAN_LOGPROB;
+          else if (lp[k] > 0.0f) fl |= GRW_FLAG_POS_LOGPROB;
+        }
+      }
+      block_append<8>(buf, &cnt_s, e, ne);
+      lds_barrier();
       n = cnt_s;
+    };
+    int c0[8], c1[8];
+    float l0[8], l1[8], t0[8], t1[8];
+    load_round(0, c0, l0, t0);
+    for (int base = 0; base < cnt; base += 2 * kLongChunk) {
+      if (base + kLongChunk < cnt) load_round(base + kLongChunk, c1, l1, t1);
+      run_round(c0, l0, t0);
+      if (base + kLongChunk >= cnt) break;
+      if (base + 2 * kLongChunk < cnt) load_round(base + 2 * kLongChunk, c0, l0, t0);
+      run_round(c1, l1, t1);
     }
     uint64_t T = 1;
     n_out = n;
