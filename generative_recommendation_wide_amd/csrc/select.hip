@@ -1617,7 +1617,8 @@ __global__ __launch_bounds__(256) void select_pilot_beam_kernel(SelArgs a) {
   } else if (b.live) {
     fl |= lfl;
   }
-  const uint64_t w = wait_sync(a, b.r, kSyncBound, &word_s);
+  // a dead or non-expanding slot keeps nothing and needs no bound (b.live is uniform)
+  const uint64_t w = b.live ? wait_sync(a, b.r, kSyncBound, &word_s) : 0ull;
   b.tau = (w & kSyncBound) ? (uint32_t)w : 0u;
   // every slot computes its own row lse (a pilot slot's equals its pilot's: same layout, same
   // reduction order)
