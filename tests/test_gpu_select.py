@@ -156,3 +156,17 @@ def test_bound_wait_fallback_keeps_result(lib, case):
         raw = [v.astype(np.float32) for v in x]
         select_loop_vs_oracle(lib, W, K, C, S, lambda d: raw[d], None, label="wait0-logits", wait_limit=0,
                               raw_logits=True)
+
+
+def test_wide_request_long_rows_with_pilot_bound(lib):
+    """A request wider than the register-resident path's pilot capacity on the general
+    kernels (W = 4500, top_k = 32, rows of 9000 codes): its own pilot set gives a bound, the
+    rows stream through the LDS buffer in prefetched rounds, and the selection stays
+    bit-exact; the bound keeps the pool far below W * top_k."""
+    W, K, C, S = [4500], [32], 9000, 2
+    rng = np.random.default_rng(31)
+    lps = [np.minimum(rng.standard_normal((W[0], C)).astype(np.float32) * 3 - 9, 0) for _ in range(S)]
+    say("[select] W = 4500, K = 32, C = 9000 (general kernels, fan-out first step)")
+    loop, ws = select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wide-long", fanout=True)
+    assert int((loop.parents[1] >= 0).sum().item()) == W[0]
+    assert loop.pool_sizes[0][-1] < W[0] * K[0] // 8, loop.pool_sizes
