@@ -1,13 +1,14 @@
 // Unshared stage and merge of beam attention (xLLM generative-recommendation design doc,
 // section 4.2.2 stages 2 and 3; section 4.2.1 for the token-granular decode KV).
 //
-// Unshared stage: one wavefront per beam slot.  The wave walks the beam's parent
-// pointers (j_d = b, j_{e-1} = parent[e][j_e]) and attends to the d + 1 decode tokens of
-// its ancestry directly where they were written — no block copy, no reorder of the decode
-// KV after selection.  Each lane holds E = Hkv*D/64 contiguous elements of the token's
-// K and V rows (one kv head spans D/E lanes) and the matching elements of the beam's G
-// query heads of that kv head; the next parent pointer is loaded together with the
-// current token's K/V so the pointer chase overlaps the KV reads.
+// Unshared stage: NW wavefronts per beam slot, each for Hkv/NW of its kv heads.  A wave
+// walks the beam's parent pointers (j_d = b, j_{e-1} = parent[e][j_e]) and attends to the
+// d + 1 decode tokens of its ancestry directly where they were written — no block copy, no
+// reorder of the decode KV after selection.  Each lane holds E = Hkv*D/(64*NW) contiguous
+// elements of the token's K and V rows (one kv head spans D/E lanes) and the matching
+// elements of the beam's G query heads of that kv head; the next parent pointer is loaded
+// together with the current token's K/V so the pointer chase overlaps the KV reads.  More
+// waves per slot give a narrow batch more loads in flight.
 //
 // Merge: per (slot, query head) the partials i (the shared stage's splits and the
 // unshared stage) combine as lse = log sum_i exp(lse_i), o = sum_i exp(lse_i - lse) o_i
@@ -70,15 +71,17 @@ __device__ __forceinline__ void load_row(const void* base, size_t off, float (&x
 
 // FUSE: merge the unshared partial with the shared stage's partials in the epilogue and
 // write `out` directly (dead slots write zeros); otherwise write the unshared partial.
-template <int KVT, int E, int G, bool FUSE>
+template <int KVT, int E, int G, int NW, bool FUSE>
 __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int slot = gw / NW;
   if (slot >= a.sumW) return;
   const int sumW = a.sumW, D = a.D, Hq = a.Hq;
   const int LPH = D / E;                 // lanes per kv head
-  const int hk = lane / LPH;             // this lane's kv head
-  const int d0 = (lane - hk * LPH) * E;  // first head-dim element of this lane
+  const int hl = lane / LPH;             // this lane's kv head within the wave's share
+  const int hk = (gw - slot * NW) * (64 / LPH) + hl;   // this lane's kv head
+  const int d0 = (lane - hl * LPH) * E;  // first head-dim element of this lane
   const int step = a.step;
 
   const int par = a.parent_idx[(size_t)step * sumW + slot];
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
       float* dst = a.ou + ((size_t)slot * Hq + hk * G + jj) * D + d0;
 #pragma unroll
       for (int i = 0; i < E; ++i) dst[i] = o[jj][i] * inv;
-      if (lane == hk * LPH) a.lu[(size_t)slot * Hq + hk * G + jj] = (m[jj] + fast_log2(l[jj])) * kLn2;
+      if (lane == hl * LPH) a.lu[(size_t)slot * Hq + hk * G + jj] = (m[jj] + fast_log2(l[jj])) * kLn2;
     }
   } else {
     // online-softmax merge with the shared partials, in log2 units:
@@ -243,34 +246,40 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   *dst = acc * (1.0f / wsum);
 }
 
-template <int KVT, int E, bool FUSE>
-hipError_t launch_unshared_g(const AttnArgs& a, hipStream_t s, int blocks) {
+template <int KVT, int E, int NW, bool FUSE>
+hipError_t launch_unshared_g(const AttnArgs& a, hipStream_t s) {
+  const int blocks = (int)(((int64_t)a.sumW * NW + 3) / 4);
   switch (a.g) {
-    case 1: attn_unshared_kernel<KVT, E, 1, FUSE><<<blocks, 256, 0, s>>>(a); break;
-    case 2: attn_unshared_kernel<KVT, E, 2, FUSE><<<blocks, 256, 0, s>>>(a); break;
-    default: attn_unshared_kernel<KVT, E, 4, FUSE><<<blocks, 256, 0, s>>>(a); break;
+    case 1: attn_unshared_kernel<KVT, E, 1, NW, FUSE><<<blocks, 256, 0, s>>>(a); break;
+    case 2: attn_unshared_kernel<KVT, E, 2, NW, FUSE><<<blocks, 256, 0, s>>>(a); break;
+    default: attn_unshared_kernel<KVT, E, 4, NW, FUSE><<<blocks, 256, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
 
+// Waves per slot: rows of 16 elements per lane (Hkv*D = 1024) go to two waves of 8 each,
+// which doubles the loads in flight per CU (one wave per slot leaves 2048 slots at two
+// waves per SIMD).
+inline int unshared_waves_per_slot(const AttnArgs& a) { return (a.Hkv * a.D) / 64 == 16 ? 2 : 1; }
+
 template <int KVT, bool FUSE>
-hipError_t launch_unshared_e(const AttnArgs& a, hipStream_t s, int blocks) {
+hipError_t launch_unshared_e(const AttnArgs& a, hipStream_t s) {
+  if (unshared_waves_per_slot(a) == 2) return launch_unshared_g<KVT, 8, 2, FUSE>(a, s);
   switch ((a.Hkv * a.D) / 64) {
-    case 2: return launch_unshared_g<KVT, 2, FUSE>(a, s, blocks);
-    case 4: return launch_unshared_g<KVT, 4, FUSE>(a, s, blocks);
-    case 8: return launch_unshared_g<KVT, 8, FUSE>(a, s, blocks);
-    default: return launch_unshared_g<KVT, 16, FUSE>(a, s, blocks);
+    case 2: return launch_unshared_g<KVT, 2, 1, FUSE>(a, s);
+    case 4: return launch_unshared_g<KVT, 4, 1, FUSE>(a, s);
+    case 8: return launch_unshared_g<KVT, 8, 1, FUSE>(a, s);
+    default: return launch_unshared_g<KVT, 16, 1, FUSE>(a, s);
   }
 }
 
 template <bool FUSE>
 hipError_t launch_unshared_t(const AttnArgs& a, hipStream_t s) {
-  const int blocks = (a.sumW + 3) / 4;
-  if (blocks == 0) return hipSuccess;
+  if (a.sumW == 0) return hipSuccess;
   switch (a.kv_dtype) {
-    case GRW_F32: return launch_unshared_e<GRW_F32, FUSE>(a, s, blocks);
-    case GRW_BF16: return launch_unshared_e<GRW_BF16, FUSE>(a, s, blocks);
-    default: return launch_unshared_e<GRW_FP8_E4M3, FUSE>(a, s, blocks);
+    case GRW_F32: return launch_unshared_e<GRW_F32, FUSE>(a, s);
+    case GRW_BF16: return launch_unshared_e<GRW_BF16, FUSE>(a, s);
+    default: return launch_unshared_e<GRW_FP8_E4M3, FUSE>(a, s);
   }
 }
 
