@@ -333,6 +333,9 @@ namespace {
 int bind_batch(grw_ws* w, int32_t n_requests, const int32_t* W_host, const int32_t* K_host, const int32_t* P_host,
                void* stream) {
   const grw_limits& L = w->lim;
+  // a failed bind leaves no batch bound: the host mirror below is rewritten before every check
+  // has passed, so later step calls must not run against it
+  w->bound = false;
   if (n_requests < 1 || n_requests > L.max_requests) return GRW_EINVAL;
   std::vector<ReqDesc> req(n_requests);
   int64_t sumW = 0, kv = 0, pool = 0;

@@ -321,6 +321,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
 
     // O^T += V^T P^T
     const __bf16* vt = sv0 + buf * V_TILE;
+    const bool tail = p + NT > p1;   // keys >= p1 in this tile: storage padding or the next split
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -330,7 +331,13 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
         const __bf16* row = vt + (db * 32 + l32) * VS;
         const bf16x4 v0 = *(const bf16x4*)(row + kb0);
         const bf16x4 v1 = *(const bf16x4*)(row + kb0 + 8);
-        const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        if (tail) {
+          // p = 0 there, but padding may hold any bits (0 * NaN = NaN): those values become 0
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (p + kb0 + (e >> 2) * 8 + (e & 3) >= p1) av[e] = (__bf16)0.0f;
+        }
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[db], 0, 0, 0);
       }
     }
@@ -624,6 +631,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
       }
       const uint8_t* pp = smem + PBUF + bt * P_WAVE;
       const uint8_t* vt = smem + VRING + ((i - 1) & 1) * TILE_BYTES;
+      const int pt = p0 + (i - 1) * NT;          // first key of the tile
+      const bool tail = pt + NT > p1;            // wave-uniform: the split's last, partial tile
       bf16x8 pf[2][4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -639,6 +648,15 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
           for (int db = 0; db < DH / 32; ++db) {
             const int d = db * 32 + l32;
             vf[k2][db] = *(const bf16x8*)(vt + d * 128 + ((lc ^ ((d >> 1) & 7)) << 4));
+          }
+          if (tail) {
+            // keys >= p1 (storage padding or the next split) have p = 0, but padding may hold
+            // any bits (0 * NaN = NaN): their values become 0.  Chunk lc holds keys 8 lc .. 8 lc + 7.
+#pragma unroll
+            for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (pt + lc * 8 + e >= p1) vf[k2][db][e] = (__bf16)0.0f;
           }
         }
         __builtin_amdgcn_s_setprio(1);

@@ -1455,7 +1455,15 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
     if constexpr (L == kTrie) {
       if (b.mask == nullptr) return b.beg + (int)threadIdx.x + 256 * k;
       const int c = rr.code[k];
-      return b.beg + (int)mprefix[c >> 5] + __builtin_popcount(mwords[c >> 5] & ((1u << (c & 31)) - 1u));
+      const int e = b.beg + (int)mprefix[c >> 5] + __builtin_popcount(mwords[c >> 5] & ((1u << (c & 31)) - 1u));
+      // a mask bit must name a code of the CSR row: the rank is that code's edge.  Otherwise
+      // the code is no child of the node; the W-of-pool stage's search then finds no child
+      // either (node -1) and both flag it
+      if (e >= b.beg + b.cnt || a.code[e] != c) {
+        fl |= GRW_FLAG_CHILD_MISSING;
+        return -1;
+      }
+      return e;
     } else {
       return -1;
     }

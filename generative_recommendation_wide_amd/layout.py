@@ -30,16 +30,18 @@ def stored_tensor(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return _torch_view(a, dtype).to(device)
 
 
-def pack_shared_kv(k_list, v_list, dtype: str, device="cuda"):
+def pack_shared_kv(k_list, v_list, dtype: str, device="cuda", pad=0):
     """Pack per-request prompt KV arrays ([Hkv][P_r][D] each, stored format) into the
-    library's per-layer buffers (k: [Hkv][Pp][D] blocks, v: [Hkv][D][Pp] blocks)."""
+    library's per-layer buffers (k: [Hkv][Pp][D] blocks, v: [Hkv][D][Pp] blocks).  ``pad`` is
+    the stored value (element bits for bf16 and fp8) written to the padding rows, which the
+    library ignores whatever they hold."""
     kb, vb = [], []
     for k, v in zip(k_list, v_list):
         Hkv, P, D = k.shape
         Pp = (P + PAD_P - 1) // PAD_P * PAD_P
-        kp = np.zeros((Hkv, Pp, D), dtype=k.dtype)
+        kp = np.full((Hkv, Pp, D), pad, dtype=k.dtype)
         kp[:, :P] = k
-        vp = np.zeros((Hkv, D, Pp), dtype=v.dtype)
+        vp = np.full((Hkv, D, Pp), pad, dtype=v.dtype)
         vp[:, :, :P] = np.transpose(v, (0, 2, 1))
         kb.append(kp.reshape(-1))
         vb.append(vp.reshape(-1))

@@ -140,15 +140,18 @@ int grw_beams_init(grw_ws* ws, float* beam_scores, int32_t* beam_node, void* str
  *
  * Three stages run on `stream`: the shared stage (each prompt KV tile streamed once per
  * beam group into LDS and reused by all of the request's beams, bf16 MFMA when D = 128
- * and q is bf16), the unshared stage (one wavefront per beam walking parent pointers),
+ * and q is bf16), the unshared stage (wavefronts walking each beam's parent pointers: one
+ * per beam slot, or two when Hkv * D = 1024, each then taking half of the slot's kv heads),
  * and the online-softmax merge of their partial outputs and log-sum-exp statistics.
  *
  *   q          [sumW][Hq][D]  q_dtype
  *   k_shared   prompt keys of this layer, requests packed back to back: request r's block
  *              is [Hkv][Pp_r][D] at element offset Hkv*D*(Pp_0 + ... + Pp_{r-1}),
- *              Pp_r = P_r rounded up to a multiple of 64 (rows >= P_r are ignored)
+ *              Pp_r = P_r rounded up to a multiple of 64 (rows >= P_r are ignored and may
+ *              hold any bits, NaN included)
  *   v_shared   prompt values of this layer, same packing, each block TRANSPOSED:
- *              [Hkv][D][Pp_r] (the PV contraction streams it without a transpose)
+ *              [Hkv][D][Pp_r] (the PV contraction streams it without a transpose); columns
+ *              >= P_r are ignored like the key rows
  *   k_scale, v_scale  [Hkv] float per-head scales (GRW_FP8_E4M3 only, else NULL); the
  *              value of an fp8 code is code * scale
  *   k_unshared, v_unshared  [>= step + 1][sumW][Hkv][D]  kv_dtype: the decode token of
@@ -297,7 +300,8 @@ int beam_select_logits(grw_ws* ws, const float* logits, const float* noise, floa
  *   dense_slot  [n_internal] int32: index of the node's mask, or -1 (CSR only); NULL: none
  *   dense_mask  [n_dense][(C + 31) / 32] uint32: bit c % 32 of word c / 32 is set when code
  *               c is a child of the node (must agree with the CSR row; a code set here but
- *               missing from the CSR row raises GRW_FLAG_CHILD_MISSING)
+ *               missing from the CSR row that the selection keeps raises
+ *               GRW_FLAG_CHILD_MISSING, and its output node is -1)
  */
 typedef struct grw_trie {
   const int32_t* row_ptr;

@@ -47,7 +47,7 @@ def ancestry(parents: np.ndarray, step: int, b: int):
 
 
 def oracle_attention(q, k_s, v_s, k_u, v_u, parents, step, *, q_dtype, kv_dtype,
-                     k_scale=None, v_scale=None, beams=None):
+                     k_scale=None, v_scale=None, beams=None, threads=1):
     """Attention output of one request at one layer and decode depth ``step``.
 
     q        [W][Hq][D]          stored (f32 / bf16 bits) — this request's slots
@@ -56,6 +56,7 @@ def oracle_attention(q, k_s, v_s, k_u, v_u, parents, step, *, q_dtype, kv_dtype,
     parents  [S][W] int          request-local parent slot per depth (negative = dead)
     k_scale, v_scale [Hkv]       fp8 scales (kv_dtype == "fp8")
     beams    iterable of slots to evaluate (default: all)
+    threads  beams evaluated at once (a thread pool; each beam's arithmetic is the same)
 
     Returns float64 [len(beams)][Hq][D].
     """
@@ -69,9 +70,11 @@ def oracle_attention(q, k_s, v_s, k_u, v_u, parents, step, *, q_dtype, kv_dtype,
     Vs = decode_stored(v_s, kv_dtype, None if vsc is None else vsc[:, None, None])
     beams = list(range(W)) if beams is None else [int(b) for b in beams]
     out = np.zeros((len(beams), Hq, D), np.float64)
-    for i, b in enumerate(beams):
+
+    def one(i):
+        b = beams[i]
         if parents[step][b] < 0:
-            continue                                  # dead slot: zero output
+            return                                    # dead slot: zero output
         js = ancestry(parents, step, b)
         ku = np.stack([k_u[e][j] for e, j in enumerate(js)], axis=1)   # [Hkv][d+1][D]
         vu = np.stack([v_u[e][j] for e, j in enumerate(js)], axis=1)
@@ -82,4 +85,12 @@ def oracle_attention(q, k_s, v_s, k_u, v_u, parents, step, *, q_dtype, kv_dtype,
         qb = decode_stored(q[b], q_dtype)             # [Hq][D]
         for h in range(Hq):
             out[i, h] = attend_concat(qb[h], Kcat[h // g], Vcat[h // g])
+
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(len(beams))))
+    else:
+        for i in range(len(beams)):
+            one(i)
     return out

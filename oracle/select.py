@@ -62,7 +62,8 @@ def _is_member(sorted_set: np.ndarray, keys: np.ndarray) -> np.ndarray:
     return (idx < sorted_set.size) & (sorted_set[idx_c] == keys)
 
 
-def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=None, temperature=0.0):
+def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=None, temperature=0.0,
+                  threads=1):
     """One selection step of one request.
 
     lp        float32 [Wslots][C]   log-probabilities of this step
@@ -73,6 +74,8 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=
     prefix_sets  output of catalog_prefix_sets, or None when unconstrained
     noise     float32 [Wslots][C] Gumbel draws of the sampled selection, or None
     temperature  T >= 0 of the sampled selection (T = 0 orders by the key alone)
+    threads   beams whose per-beam sort runs at once (a thread pool: numpy releases the
+              interpreter lock inside its sorts); every beam's arithmetic is the same
 
     Returns a dict: tokens int32 [W], parents int32 [W], scores float32 [W],
     prefixes (list of packed prefixes, None for pad slots) and pool_size (the number of
@@ -87,11 +90,12 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=
         noise = np.asarray(noise, dtype=np.float32)
         assert np.isfinite(noise).all()
     all_codes = np.arange(C, dtype=np.int64)
-    pool_key, pool_okey, pool_flat = [], [], []
-    for b in range(scores.shape[0]):
+
+    def beam_top_k(b):
+        """Beam b's top_k candidates (keys, ordering keys, flat indices), or None."""
         s = scores[b]
         if s == NEG_INF:
-            continue
+            return None
         codes = all_codes
         if prefix_sets is not None:
             codes = all_codes[_is_member(prefix_sets[level + 1], prefixes[b] * C + all_codes)]
@@ -103,9 +107,19 @@ def oracle_select(lp, scores, prefixes, level, K, W, C, prefix_sets=None, noise=
         live = (keys != NEG_INF) & (okeys != NEG_INF)
         codes, keys, okeys = codes[live], keys[live], okeys[live]
         order = np.lexsort((codes, -okeys))[:K]       # full stable sort, keep top_k
-        pool_key.append(keys[order])
-        pool_okey.append(okeys[order])
-        pool_flat.append(b * C + codes[order])
+        return keys[order], okeys[order], b * C + codes[order]
+
+    beams = range(scores.shape[0])
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(beam_top_k, beams))
+    else:
+        parts = [beam_top_k(b) for b in beams]
+    parts = [x for x in parts if x is not None]
+    pool_key = [x[0] for x in parts]
+    pool_okey = [x[1] for x in parts]
+    pool_flat = [x[2] for x in parts]
     tokens = np.full(W, -1, np.int32)
     parents = np.full(W, -1, np.int32)
     out_scores = np.full(W, NEG_INF, np.float32)

@@ -335,7 +335,30 @@ def _log_softmax_f32(x: np.ndarray) -> np.ndarray:
     return np.minimum((x - lse).astype(np.float32), np.float32(0.0))
 
 
-def logprob_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None):
+def _ultra_row(seed: int, wl: Workload, base: int, src: int) -> np.ndarray:
+    """Row ``src`` of base matrix ``base`` of the ultra-wide workload (its own stream)."""
+    g = _rng(seed, wl, _S_LOGITS, base, int(src))
+    return _log_softmax_f32(g.standard_normal(wl.C) * wl.logit_sigma)
+
+
+@functools.lru_cache(maxsize=2)
+def _ultra_base(wl: Workload, seed: int, base: int, threads: int) -> np.ndarray:
+    """Whole base matrix [W][C] of the ultra-wide workload, rows drawn by a thread pool (each
+    row has its own generator, so the values do not depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+    W = int(request_shapes(wl, seed)[0].sum())
+    out = np.empty((W, wl.C), np.float32)
+
+    def fill(lo):
+        for i in range(lo, min(W, lo + 64)):
+            out[i] = _ultra_row(seed, wl, base, i)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(0, W, 64)))
+    return out
+
+
+def logprob_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None, threads: int = 1):
     """Log-probabilities [sumW][C] float32 of one decode step.
 
     logits ~ N(0, sigma) per (step, slot) row (sigma is the standard deviation), then
@@ -343,7 +366,9 @@ def logprob_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None)
 
     The ultra-wide workload uses two base matrices; step d uses base d % 2 with its rows
     rotated by 7919 * d mod W (so 16 steps need only 2 x 2.8 GiB of host data).
-    ``rows`` optionally selects a subset of slot rows.
+    ``rows`` optionally selects a subset of slot rows.  For the ultra-wide workload without
+    ``rows``, the step's base matrix is drawn once (by ``threads`` threads) and kept for the
+    step of the same parity.
     """
     W, K, P = shapes if shapes is not None else request_shapes(wl, seed)
     sumW = int(W.sum())
@@ -351,13 +376,13 @@ def logprob_rows(wl: Workload, step: int, seed: int = 0, shapes=None, rows=None)
         base = step % 2
         shift = (7919 * step) % sumW
         idx = (np.arange(sumW) - shift) % sumW      # row i of step d = base row (i - shift)
-        if rows is not None:
-            idx = idx[np.asarray(rows)]
+        if rows is None:
+            return _ultra_base(wl, seed, base, threads)[idx]
+        idx = idx[np.asarray(rows)]
         out = np.empty((idx.size, wl.C), np.float32)
         # each base row has its own stream, so rows can be drawn independently
         for i, src in enumerate(idx):
-            g = _rng(seed, wl, _S_LOGITS, base, int(src))
-            out[i] = _log_softmax_f32(g.standard_normal(wl.C) * wl.logit_sigma)
+            out[i] = _ultra_row(seed, wl, base, int(src))
         return out
     g = _rng(seed, wl, _S_LOGITS, step)
     x = g.standard_normal((sumW, wl.C)) * wl.logit_sigma

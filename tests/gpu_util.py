@@ -2,6 +2,7 @@
 through its binding, and compare with the oracle."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -15,6 +16,12 @@ from synth import build_trie_csr
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def oracle_threads() -> int:
+    """Threads for the oracle's per-beam loops: the host cores this process may use, at most
+    16 (the share of one GPU's host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def make_ws(lib, Ws, Ks, Ps, *, C, S, Hq=16, Hkv=8, D=128, q_dtype="bf16", kv_dtype="bf16",
@@ -42,13 +49,14 @@ def trie_device(trie, lib=None, C=None, dense_min_fanout=None):
 
 def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None, label="",
                           noise_of_step=None, temperature=0.0, raw_logits=False, dense_min_fanout=None,
-                          fanout=False, wait_limit=None):
+                          fanout=False, wait_limit=None, threads=1):
     """Run S beam_select steps on the GPU (its own outputs feeding the next step) and compare
     every checked request bit-exactly with oracle_select at every step.  With noise_of_step,
     the steps are the Gumbel-sampled selection at the given temperature; with raw_logits,
     lp_of_step returns raw logits and the steps fuse their log-softmax; with fanout, the first
     step is the first-step fan-out, whose oracle is the selection with top_k = W; with
-    wait_limit, the workspace's bound-wait limit.  Returns the loop."""
+    wait_limit, the workspace's bound-wait limit; threads: the oracle's per-beam thread pool.
+    Returns the loop."""
     Ws, Ks = list(map(int, Ws)), list(map(int, Ks))
     R = len(Ws)
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
@@ -78,7 +86,7 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
             scores, prefixes = state[r]
             sel = oracle_select_logits if raw_logits else oracle_select
             res = sel(lp[a:a + W], scores, prefixes, d, W if fanout and d == 0 else Ks[r], W, C, psets,
-                      None if g is None else g[a:a + W], temperature)
+                      None if g is None else g[a:a + W], temperature, **({"threads": threads} if not raw_logits else {}))
             where = f"{label} step {d} request {r}"
             np.testing.assert_array_equal(tok[a:a + W], res["tokens"], err_msg=where + " tokens")
             np.testing.assert_array_equal(par[a:a + W], res["parents"], err_msg=where + " parents")
@@ -104,10 +112,11 @@ def select_loop_vs_oracle(lib, Ws, Ks, C, S, lp_of_step, items=None, check=None,
     return loop, ws
 
 
-def upload_layer(layer, wl_dtype_q, wl_dtype_kv, device="cuda"):
-    """Synthetic layer (synth.attention_layer output) -> device tensors in library layout."""
+def upload_layer(layer, wl_dtype_q, wl_dtype_kv, device="cuda", pad=0):
+    """Synthetic layer (synth.attention_layer output) -> device tensors in library layout;
+    ``pad`` fills the prompt storage padding."""
     lib_layout = sys.modules["generative_recommendation_wide_amd"]
-    k_s, v_s = lib_layout.pack_shared_kv(layer["k_s"], layer["v_s"], wl_dtype_kv, device)
+    k_s, v_s = lib_layout.pack_shared_kv(layer["k_s"], layer["v_s"], wl_dtype_kv, device, pad=pad)
     out = dict(q=lib_layout.stored_tensor(layer["q"], wl_dtype_q, device),
                k_s=k_s, v_s=v_s,
                k_u=lib_layout.stored_tensor(layer["k_u"], wl_dtype_kv, device),
@@ -117,7 +126,7 @@ def upload_layer(layer, wl_dtype_q, wl_dtype_kv, device="cuda"):
     return out
 
 
-def attention_vs_oracle(out_gpu, layer, parents, step, Ws, q_dtype, kv_dtype, samples, tol, label=""):
+def attention_vs_oracle(out_gpu, layer, parents, step, Ws, q_dtype, kv_dtype, samples, tol, label="", threads=1):
     """Compare sampled slots of the GPU output [sumW][Hq][D] with oracle_attention."""
     boff = np.concatenate([[0], np.cumsum(Ws)[:-1]]).astype(int)
     worst = 0.0
@@ -129,7 +138,7 @@ def attention_vs_oracle(out_gpu, layer, parents, step, Ws, q_dtype, kv_dtype, sa
         ref = oracle_attention(layer["q"][step][a:a + W], layer["k_s"][r], layer["v_s"][r],
                                layer["k_u"][:, a:a + W], layer["v_u"][:, a:a + W], parents[:, a:a + W],
                                step, q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=layer["k_scale"],
-                               v_scale=layer["v_scale"], beams=beams)
+                               v_scale=layer["v_scale"], beams=beams, threads=threads)
         got = out_gpu[a + np.array(beams)].astype(np.float64)
         err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
         worst = max(worst, err)

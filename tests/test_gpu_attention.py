@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from synth import attention_layer, random_parents, request_shapes, workload
-from tests.gpu_util import attention_vs_oracle, make_ws, say, upload_layer
+from tests.gpu_util import attention_vs_oracle, make_ws, oracle_threads, say, upload_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -15,11 +15,11 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 2e-2}
 
 
 def run_attention(lib, wl, layer, parents, Ws, Ks, Ps, steps, samples_of_step, max_splits=0,
-                  Hq=None, Hkv=None, D=None):
+                  Hq=None, Hkv=None, D=None, pad=0):
     Hq, Hkv, D = Hq or wl.Hq, Hkv or wl.Hkv, D or wl.D
     ws = make_ws(lib, Ws, Ks, Ps, C=16, S=wl.S, Hq=Hq, Hkv=Hkv, D=D, q_dtype=wl.q_dtype,
                  kv_dtype=wl.kv_dtype, max_splits=max_splits)
-    dev = upload_layer(layer, wl.q_dtype, wl.kv_dtype)
+    dev = upload_layer(layer, wl.q_dtype, wl.kv_dtype, pad=pad)
     par = torch.from_numpy(parents).cuda()
     out = torch.empty(int(sum(Ws)), Hq, D, dtype=torch.float32, device="cuda")
     worst = 0.0
@@ -32,8 +32,10 @@ def run_attention(lib, wl, layer, parents, Ws, Ks, Ps, steps, samples_of_step, m
         # dead slots are exactly zero
         dead = np.nonzero(parents[d] < 0)[0]
         assert np.all(o[dead] == 0.0)
+        say(f"[attn] {wl.name} d={d}: comparing with the oracle")
         worst = max(worst, attention_vs_oracle(o, layer, parents, d, list(Ws), wl.q_dtype, wl.kv_dtype,
-                                               samples_of_step(d), TOL[wl.kv_dtype], label=f"{wl.name} d={d}"))
+                                               samples_of_step(d), TOL[wl.kv_dtype], label=f"{wl.name} d={d}",
+                                               threads=oracle_threads()))
     assert ws.error_flags() == 0
     say(f"[attn] {wl.name}: worst max-abs error {worst:.3e}")
     return ws
@@ -68,6 +70,55 @@ def test_wide512_sampled(lib):
     rng = np.random.default_rng(1)
     samples = lambda d: {r: rng.choice(512, size=24, replace=False) for r in range(len(W))}
     run_attention(lib, wl, layer, par, W, K, P, range(wl.S), samples)
+
+
+def short_prompt_case(name, P, index):
+    """A workload's attention shape with a short prompt, so that the decode tokens carry a
+    large share of the softmax mass (a wrong ancestor or merge weight then moves the output far
+    beyond the tolerance; tests/test_oracle_attention.py checks that on these inputs)."""
+    import dataclasses
+    wl = dataclasses.replace(workload(name), P=P, layers=1, index=index)
+    W, K, Ps = request_shapes(wl)
+    return wl, (W, K, Ps)
+
+
+def test_wide512_short_prompt_every_slot(lib):
+    """The headline attention shape (4 requests x W = 512, 16/8/128 bf16: two waves per slot in
+    the unshared stage, slots up to 2047) with a 64-token prompt: every slot at depths 0-2
+    against the oracle."""
+    wl, shapes = short_prompt_case("wide512", 64, 60)
+    W, K, P = shapes
+    layer = attention_layer(wl, 0, shapes=shapes)
+    par = random_parents(wl, shapes=shapes, dead_frac=0.05)
+    run_attention(lib, wl, layer, par, W, K, P, range(wl.S), all_slots(W))
+
+
+def test_ultra5000_short_prompt_deep_every_slot(lib):
+    """The ultra-wide attention shape (W = 5000) with a 64-token prompt: every slot walks 15
+    parent pointers at depth 15 (and 3 at depth 3) and every slot is compared."""
+    wl, shapes = short_prompt_case("ultra5000", 64, 61)
+    W, K, P = shapes
+    layer = attention_layer(wl, 0, shapes=shapes)
+    par = random_parents(wl, shapes=shapes)
+    run_attention(lib, wl, layer, par, W, K, P, [3, 15], all_slots(W))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_nan_padding_is_ignored(lib, kv):
+    """Prompt storage padding (rows P_r .. Pp_r - 1 of K, columns of V^T) filled with NaN bit
+    patterns (bf16 0x7FC0, e4m3 0x7F): the outputs are finite and match the oracle, on the
+    8-wave wide kernel (bf16 W = 300, split prompt), the 4-wave kernel (narrow bf16 and every
+    fp8 request) and prompts whose last tile is partial."""
+    import dataclasses
+    wl = dataclasses.replace(workload("mixed_fp8" if kv == "fp8" else "qwen06b"), n_requests=3, W=None, K=None,
+                             P=None, S=3, index=70 + (kv == "fp8"))
+    Ws = np.array([300, 20, 129], np.int32)
+    Ps = np.array([1000, 77, 130], np.int32)
+    Ks = Ws.copy()
+    layer = attention_layer(wl, 0, shapes=(Ws, Ks, Ps))
+    par = random_parents(wl, shapes=(Ws, Ks, Ps), dead_frac=0.1)
+    pad = 0x7FC0 if kv == "bf16" else 0x7F
+    run_attention(lib, wl, layer, par, Ws, Ks, Ps, [0, 2], all_slots(Ws), max_splits=4, pad=pad)
 
 
 def test_mixed_fp8_ragged(lib):

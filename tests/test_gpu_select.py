@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from synth import catalog_items, logprob_rows, request_shapes, workload
-from tests.gpu_util import say, select_loop_vs_oracle
+from tests.gpu_util import oracle_threads, say, select_loop_vs_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -170,3 +170,22 @@ def test_wide_request_long_rows_with_pilot_bound(lib):
     loop, ws = select_loop_vs_oracle(lib, W, K, C, S, lambda d: lps[d], None, label="wide-long", fanout=True)
     assert int((loop.parents[1] >= 0).sum().item()) == W[0]
     assert loop.pool_sizes[0][-1] < W[0] * K[0] // 8, loop.pool_sizes
+
+
+def test_ultra5000_select_at_its_shape(lib):
+    """The ultra-wide workload's selection at its real shape: one request, W = 5000, top_k =
+    64, unconstrained rows of 151936 codes (the general kernels: rows longer than 8192 codes,
+    W > 1024, the wide pilot set).  Steps 0-3 take the live beams 1 -> 64 -> 4096 -> 5000 ->
+    5000; every step is bit-exact against the oracle fed the checked state."""
+    import synth.workloads as sw
+    wl = workload("ultra5000")
+    W, K, P = request_shapes(wl)
+    th = oracle_threads()
+    say(f"[select] ultra5000 shape: W={W[0]} K={K[0]} C={wl.C}, 4 steps, oracle on {th} threads")
+    try:
+        loop, ws = select_loop_vs_oracle(lib, W, K, wl.C, 4, lambda d: logprob_rows(wl, d, threads=th), None,
+                                         label="ultra5000", threads=th)
+    finally:
+        sw._ultra_base.cache_clear()
+    live = [int((loop.parents[d] >= 0).sum().item()) for d in range(4)]
+    assert live == [64, 4096, 5000, 5000], live

@@ -195,3 +195,40 @@ def test_fp8_and_bf16_inputs_decode_through_scales():
         ref = torch.nn.functional.scaled_dot_product_attention(
             Q, Kc.repeat_interleave(2, 0), Vc.repeat_interleave(2, 0))[:, 0].numpy()
         np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name,P,index,step", [("wide512", 64, 60, 2), ("ultra5000", 64, 61, 15)])
+def test_short_prompt_cases_see_the_decode_tokens(name, P, index, step):
+    """The GPU parity cases with a 64-token prompt (tests/test_gpu_attention.py) can tell a
+    right answer from the mistakes the unshared stage and the merge could make: on the same
+    inputs, a wrong ancestor at one depth, or the decode-token partial left out of the merge,
+    moves the oracle's output by more than five times the 2e-2 tolerance on every sampled slot.
+    (At the full 4096-token prompt the same mistakes stay below the tolerance.)"""
+    import dataclasses
+
+    from synth import attention_layer, random_parents, request_shapes, workload
+    wl = dataclasses.replace(workload(name), P=P, layers=1, index=index)
+    W, K, Ps = request_shapes(wl)
+    shapes = (W, K, Ps)
+    layer = attention_layer(wl, 0, shapes=shapes, requests=[0])
+    par = random_parents(wl, shapes=shapes, dead_frac=0.05 if name == "wide512" else 0.0)
+    Wr = int(W[0])
+    rng = np.random.default_rng(9)
+    beams = [int(b) for b in rng.choice(np.nonzero(par[step, :Wr] >= 0)[0], size=12, replace=False)]
+    args = (layer["q"][step][:Wr], layer["k_s"][0], layer["v_s"][0], layer["k_u"][:, :Wr], layer["v_u"][:, :Wr])
+    right = oracle_attention(*args, par[:, :Wr], step, q_dtype="bf16", kv_dtype="bf16", beams=beams)
+    # a wrong ancestor: every parent pointer at depth `step` moved to another live slot
+    wrong = par[:, :Wr].copy()
+    live = np.nonzero(par[step - 1, :Wr] >= 0)[0] if step > 1 else np.arange(Wr)
+    for b in beams:
+        wrong[step, b] = int(live[(np.searchsorted(live, wrong[step, b]) + 1) % live.size])
+    moved = oracle_attention(*args, wrong, step, q_dtype="bf16", kv_dtype="bf16", beams=beams)
+    # the decode tokens left out: attention over the prompt alone
+    prompt_only = np.stack([
+        np.stack([attend_concat(decode_stored(args[0][b][h], "bf16"),
+                                decode_stored(args[1][h // 2], "bf16"), decode_stored(args[2][h // 2], "bf16"))
+                  for h in range(wl.Hq)]) for b in beams])
+    d_anc = np.abs(moved - right).max(axis=(1, 2))
+    d_merge = np.abs(prompt_only - right).max(axis=(1, 2))
+    assert np.all(d_anc > 0.1), d_anc
+    assert np.all(d_merge > 0.1), d_merge
