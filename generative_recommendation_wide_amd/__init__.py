@@ -153,6 +153,19 @@ def beam_select(ws: Workspace, logprobs, beam_scores, beam_node, trie_row_ptr, t
         _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"), _stream(stream)))
 
 
+def beam_select_noalloc(logprobs, beam_scores, beam_node, trie_row_ptr, trie_code, trie_n_internal: int, W: int,
+                        K: int, C: int, out_token, out_parent, out_score, out_node, device_flags=None, stream=None):
+    """beam_select of one request without a workspace: its scratch is the library's static
+    device array, so the call allocates nothing (see include/grw.h)."""
+    _lib.check("beam_select_noalloc", _L.beam_select_noalloc(
+        _ptr(logprobs, _F32, "logprobs"), _ptr(beam_scores, _F32, "beam_scores"),
+        _ptr(beam_node, _I32, "beam_node"), _ptr(trie_row_ptr, _I32, "trie_row_ptr"),
+        _ptr(trie_code, _I32, "trie_code"), int(trie_n_internal), int(W), int(K), int(C),
+        _ptr(out_token, _I32, "out_token"), _ptr(out_parent, _I32, "out_parent"),
+        _ptr(out_score, _F32, "out_score"), _ptr(out_node, _I32, "out_node"),
+        _ptr(device_flags, _I32, "device_flags"), _stream(stream)))
+
+
 def beam_select_gumbel(ws: Workspace, logprobs, noise, temperature: float, beam_scores, beam_node,
                        trie_row_ptr, trie_code, trie_n_internal: int, W: int, K: int, C: int,
                        out_token, out_parent, out_score, out_node, stream=None):

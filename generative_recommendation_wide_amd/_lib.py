@@ -23,7 +23,8 @@ EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_i
             "beam_attn_decode", "beam_attn_decode_stages", "beam_attn_decode_overlap", "beam_select", "beam_select_gumbel",
             "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_plan_batches", "grw_backtrack",
             "grw_ws_error",
-            "grw_ws_splits", "grw_ws_pool_size", "grw_ws_set_wait_limit", "grw_status_str"]
+            "grw_ws_splits", "grw_ws_pool_size", "grw_ws_set_wait_limit", "grw_status_str",
+            "beam_select_noalloc"]
 
 
 class GrwLimits(ctypes.Structure):
@@ -83,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "grw_ws_splits": [vp, i32, ctypes.POINTER(i32)],
         "grw_ws_pool_size": [vp, i32, vp, ctypes.POINTER(ctypes.c_int64)],
         "grw_ws_set_wait_limit": [vp, i32],
+        "beam_select_noalloc": [fp, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp, i32p, i32p, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

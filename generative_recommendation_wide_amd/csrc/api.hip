@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -217,6 +218,87 @@ void build_valu_work(grw_ws* w, std::vector<ShWork>& out) {
           out.push_back({ri, qh, b, s, p0, p1, 0, 0});
         }
   }
+}
+
+}  // namespace
+
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free selection of one request (beam_select_noalloc).  Its scratch — the
+// request descriptor, slot map, pilot descriptors and buffer, candidate pool and CSR edges,
+// survivor counts, bound, step words and flag word — lives in one file-scope device array
+// that each GPU holds until the process ends.  Host code never names the array in a device
+// context: its device address is looked up once per device with hipGetSymbolAddress and that
+// pointer is what the kernels receive.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kNaMaxW = 1024;                 // the register-resident selection's width limit
+constexpr int kNaMaxPool = 512 * 512;         // W * top_k entries of the candidate pool
+constexpr int kNaMaxDevices = 64;
+
+// byte offsets inside the scratch array (each 256-byte aligned)
+constexpr size_t kNaReq = 0;
+constexpr size_t kNaSlotReq = 256;
+constexpr size_t kNaPilotDesc = kNaSlotReq + sizeof(int32_t) * kNaMaxW;
+constexpr size_t kNaPilotBuf = kNaPilotDesc + sizeof(int32_t) * 4 * kMaxPilots;
+constexpr size_t kNaPool = kNaPilotBuf + sizeof(uint64_t) * kPilotCap;
+constexpr size_t kNaPoolEdge = kNaPool + sizeof(uint64_t) * kNaMaxPool;
+constexpr size_t kNaSurv = kNaPoolEdge + sizeof(int32_t) * kNaMaxPool;
+constexpr size_t kNaSync = kNaSurv + sizeof(int32_t) * kNaMaxW;
+constexpr size_t kNaWords = kNaSync + sizeof(uint64_t) * kSyncCopies * kSyncStride;   // bound, count, flags
+constexpr size_t kNaBytes = kNaWords + 256;
+static_assert(kNaSlotReq >= sizeof(ReqDesc) && kNaPilotDesc % 256 == 0 && kNaPilotBuf % 256 == 0 &&
+              kNaPool % 256 == 0 && kNaPoolEdge % 256 == 0 && kNaSurv % 256 == 0 && kNaSync % 256 == 0 &&
+              kNaWords % 256 == 0, "scratch sections must stay 256-byte aligned");
+
+}  // namespace
+
+// The scratch array itself (about 3.2 MiB per device).
+static __device__ __align__(256) uint8_t scratch[kNaBytes];
+
+namespace {
+
+std::mutex g_na_mutex;
+void* g_na_ptr[kNaMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on the first call on the device).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GRW_EDEVICE;
+  if (dev < 0 || dev >= kNaMaxDevices) return GRW_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_na_mutex);
+  if (g_na_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GRW_EDEVICE;
+    g_na_ptr[dev] = p;
+  }
+  *out = g_na_ptr[dev];
+  return GRW_OK;
+}
+
+// Per-call set-up inside the scratch: the descriptor, the slot map, the pilot descriptors
+// {slot, request, first pilot-buffer entry, threads per group}, and the words that must start
+// at zero (bound, pilot count, step words, flags).  One workgroup; a kernel rather than a
+// memset so that a captured graph replays it like every other node.
+__global__ __launch_bounds__(256) void noalloc_setup_kernel(uint8_t* base, ReqDesc rd, int n_pilot, int per,
+                                                            int clear_flags) {
+  const int tid = threadIdx.x;
+  if (tid == 0) *(ReqDesc*)(base + kNaReq) = rd;
+  int32_t* slot_req = (int32_t*)(base + kNaSlotReq);
+  for (int i = tid; i < rd.W; i += 256) slot_req[i] = 0;
+  int32_t* pd = (int32_t*)(base + kNaPilotDesc);
+  for (int j = tid; j < n_pilot; j += 256) {
+    pd[4 * j + 0] = j;
+    pd[4 * j + 1] = 0;
+    pd[4 * j + 2] = j * per;
+    pd[4 * j + 3] = 256 / per;
+  }
+  uint64_t* sync = (uint64_t*)(base + kNaSync);
+  for (int i = tid; i < kSyncCopies * kSyncStride; i += 256) sync[i] = 0ull;
+  uint32_t* words = (uint32_t*)(base + kNaWords);
+  if (tid < 2) words[tid] = 0u;                 // bound, pilot count
+  if (tid == 2 && clear_flags) words[2] = 0u;   // flag word (when the caller passes none)
 }
 
 }  // namespace
@@ -784,6 +866,78 @@ int grw_ws_splits(const grw_ws* w, int32_t r, int32_t* n_splits) {
   if (r < 0 || r >= w->R) return GRW_EINVAL;
   *n_splits = w->req[r].nsplit;
   return GRW_OK;
+}
+
+
+int beam_select_noalloc(const float* logprobs, const float* beam_scores, const int32_t* beam_node,
+                        const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
+                        int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
+                        float* out_score, int32_t* out_node, int32_t* device_flags, void* stream) {
+  if (!logprobs || !beam_scores || !out_token || !out_parent || !out_score || !out_node) return GRW_EINVAL;
+  const bool trie = trie_row_ptr != nullptr || trie_code != nullptr;
+  if (trie && (!trie_row_ptr || !trie_code || !beam_node || trie_n_internal < 1)) return GRW_EINVAL;
+  if (W < 1 || K < 1 || C < 1) return GRW_EINVAL;
+  if ((const void*)out_score == (const void*)beam_scores ||
+      (beam_node && (const void*)out_node == (const void*)beam_node))
+    return GRW_EINVAL;
+  if (W > kNaMaxW || C > kOnePass || K > kMaxK || (int64_t)W * K > kNaMaxPool || !select_fused_ok(C, W))
+    return GRW_EUNSUPPORTED;
+  void* sp = nullptr;
+  const int st = noalloc_scratch(&sp);
+  if (st != GRW_OK) return st;
+  uint8_t* base = (uint8_t*)sp;
+  ReqDesc rd{};
+  rd.boff = 0;
+  rd.W = W;
+  rd.K = K;
+  rd.P = 1;
+  rd.Pp = kPadP;
+  rd.nsplit = 1;
+  int per = 1;
+  rd.n_pilot = pilot_count(rd, 256, per);
+  int per_s = 1;
+  rd.n_pilot_s = pilot_count(rd, 64, per_s);
+  rd.n_pilot_w = rd.n_pilot;
+  rd.n_pilot_ws = rd.n_pilot_s;
+  rd.pilot_off = 0;
+  hipStream_t s = (hipStream_t)stream;
+  noalloc_setup_kernel<<<1, 256, 0, s>>>(base, rd, rd.n_pilot, per, device_flags == nullptr ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return GRW_EDEVICE;
+  uint32_t* words = (uint32_t*)(base + kNaWords);
+  SelArgs a{};
+  a.req = (const ReqDesc*)(base + kNaReq);
+  a.slot_req = (const int32_t*)(base + kNaSlotReq);
+  a.logprobs = logprobs;
+  a.noise = nullptr;
+  a.temp = 0.0f;
+  a.row_lse = nullptr;
+  a.lse_ready = 0;
+  a.scores = beam_scores;
+  a.nodes = beam_node;
+  a.row_ptr = trie ? trie_row_ptr : nullptr;
+  a.code = trie ? trie_code : nullptr;
+  a.n_internal = trie_n_internal;
+  a.mask_words = (C + 31) / 32;
+  a.C = C;
+  a.sumW = W;
+  a.R = 1;
+  a.pool = (uint64_t*)(base + kNaPool);
+  a.surv_count = (int32_t*)(base + kNaSurv);
+  a.pool_edge = (int32_t*)(base + kNaPoolEdge);
+  a.bound = words;
+  a.pilot_desc = (const int32_t*)(base + kNaPilotDesc);
+  a.n_pilots = rd.n_pilot;
+  a.pilot_buf = (uint64_t*)(base + kNaPilotBuf);
+  a.pilot_count = words + 1;
+  a.sync = (uint64_t*)(base + kNaSync);
+  a.wait_limit = kBoundSpin;
+  a.out_token = out_token;
+  a.out_parent = out_parent;
+  a.out_score = out_score;
+  a.out_node = out_node;
+  a.flags = device_flags != nullptr ? device_flags : (int32_t*)(words + 2);
+  return hip_status(launch_select_fused(a, s));
 }
 
 }  // extern "C"

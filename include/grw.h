@@ -6,6 +6,7 @@
  *   beam_select_gumbel the same with Gumbel-perturbed ordering keys (temperature > 0)
  *   beam_select_logits the same from raw logits, with the row log-softmax fused in
  *   beam_select_ex     every selection option at once, with a dense-or-CSR trie
+ *   beam_select_noalloc beam_select of one request with no workspace (allocates nothing)
  *   beam_attn_decode  beam attention over a shared prompt KV plus per-beam decode KV
  *                     reached through parent pointers, in three stages
  *                     (shared stage, unshared stage, online-softmax merge)
@@ -26,6 +27,7 @@
  *   - Every tensor argument is caller-owned DEVICE memory unless stated otherwise; the
  *     library never frees it.  The library allocates device memory only in grw_ws_create
  *     (and pinned host staging there); it never allocates in any other call.
+ *     beam_select_noalloc uses no workspace: its scratch is a static device array.
  *   - Every call that takes a stream enqueues its work on that stream and returns
  *     without synchronising and without any device-to-host copy, except grw_ws_bind_batch
  *     (one host-to-device upload of descriptors, then a stream synchronise) and
@@ -405,6 +407,35 @@ int grw_ws_pool_size(grw_ws* ws, int32_t r, void* stream, int64_t* pool_size);
    tighter bound on the wait.  Host-side; affects later beam_select* calls on this
    workspace.  GRW_EINVAL if polls < 0. */
 int grw_ws_set_wait_limit(grw_ws* ws, int32_t polls);
+
+/*
+ * beam_select_noalloc — for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): beam_select of ONE request
+ * with no workspace.  It calls no hipMalloc / hipFree and no allocating library routine; its
+ * scratch (request descriptor, slot map, pilot descriptors and buffer, candidate pool with
+ * CSR edges, survivor counts, bound, step words, flag word: about 3.2 MiB) is a static
+ * device array of the library, which every GPU the library runs on holds until the process
+ * ends.  The caller passes inputs and outputs only.
+ *
+ * Limits: 1 <= W <= 1024, 1 <= K, W * K <= 262144 (the W = K = 512 pool), 1 <= C <= 8192;
+ * sizes beyond them return GRW_EUNSUPPORTED, other argument errors GRW_EINVAL, both with
+ * nothing enqueued.  The selection, its tie rules, outputs and early exit are those of
+ * beam_select for a batch of one request (boff = 0, so out_parent holds slots 0..W-1).
+ * Each call first clears the scratch words that must start at zero (with a kernel, so a
+ * captured graph replays it), so consecutive calls of any sizes are independent.  Calls on
+ * one GPU share that GPU's array and the array keeps the last call's contents: calls that
+ * overlap on one GPU (two streams, two threads) race.
+ *   logprobs     [W][C] float32; beam_scores [W]; beam_node [W] (ignored when unconstrained)
+ *   trie_*       as for beam_select (both NULL for unconstrained selection)
+ *   out_*        [W] each, as for beam_select
+ *   device_flags [1] int32 device word that device precondition flags (grw_device_flag bits)
+ *                are OR'd into; NULL: they go to the library's own word in the scratch,
+ *                which the call clears and nothing reads
+ */
+int beam_select_noalloc(const float* logprobs, const float* beam_scores, const int32_t* beam_node,
+                        const int32_t* trie_row_ptr, const int32_t* trie_code, int32_t trie_n_internal,
+                        int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
+                        float* out_score, int32_t* out_node, int32_t* device_flags, void* stream);
 
 const char* grw_status_str(int status);
 
