@@ -30,20 +30,34 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+N_SIMDS = 1024                # 256 CUs x 4 SIMDs
+N_XCDS = 8                    # GRBM_GUI_ACTIVE comes back summed over the XCDs
 DOMINANT = "attn_shared_split_kernel"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_shared_split_wide512_traffic.txt")
-KERNEL_SOURCES = ["generative_recommendation_wide_amd/csrc/attn_shared.hip",
-                  "generative_recommendation_wide_amd/csrc/device_common.h",
-                  "generative_recommendation_wide_amd/csrc/grw_internal.h"]
+_CSRC = "generative_recommendation_wide_amd/csrc/"
+KERNEL_SOURCES = [_CSRC + "attn_shared.hip", _CSRC + "device_common.h", _CSRC + "grw_internal.h"]
+SELECT_SOURCES = [_CSRC + "select.hip", _CSRC + "device_common.h", _CSRC + "grw_internal.h"]
+# counter records: (kernels whose dispatches are summed, sources whose hash the record carries)
+TRAFFIC = {
+    "shared": (os.path.join(ROOT, "profiles", "attn_shared_split_wide512_traffic.txt"), [DOMINANT], KERNEL_SOURCES,
+               "wide512: one layer, 4 requests, W=K=512, P=4096",
+               "--steps 1 --warmup 1 --stage-reps 0"),
+    "select": (os.path.join(ROOT, "profiles", "beam_select_wide512u_traffic.txt"),
+               ["select_pilot_beam_kernel", "select_final_kernel"], SELECT_SOURCES,
+               "wide512u: one beam_select call, 4 requests, W=K=512, 8192 codes, every beam live, rows not in cache",
+               "--select-only --stage-reps 1"),
+}
+TRAFFIC_FILE = TRAFFIC["shared"][0]
+MFMA_FILE = os.path.join(ROOT, "profiles", "attn_shared_split_wide512_mfma.txt")
+N_COLD_SETS = 8               # select inputs rotated per call: 8 x 64 MiB > the 256 MB last-level cache
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -113,7 +127,7 @@ def setup(wl, seed, dev):
         x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
         lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
         del x
-    trie = None
+    trie = t = None
     items = catalog_items(wl, seed)
     if items is not None:
         t = build_trie_csr(items, C)
@@ -125,7 +139,7 @@ def setup(wl, seed, dev):
     loop = grw.DecodeLoop(ws, S, C, trie, device=dev)
     out = torch.empty(sumW, wl.Hq, wl.D, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    return dict(W=W, K=K, P=P, ws=ws, loop=loop, layers=layers, lps=lps, out=out, trie=trie)
+    return dict(W=W, K=K, P=P, ws=ws, loop=loop, layers=layers, lps=lps, out=out, trie=trie, trie_host=t)
 
 
 def shared_stage_work(wl, st):
@@ -155,33 +169,53 @@ def time_stage(fn, n_launch, stream):
     return e0.elapsed_time(e1) / n_launch   # ms per call
 
 
+def time_graph(fn, n_launch, stream, replays=3):
+    """Device time per call of fn: a HIP graph of n_launch calls (no host work between the
+    kernels), replayed `replays` times between HIP events on the launch stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_launch):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (replays * n_launch)
+
+
 def stage_timings(wl, st, reps):
-    """Per-call device time of each stage, HIP events on the launch stream."""
+    """Per-call device time of each stage at the last depth, every layer in turn: HIP graphs of
+    the stage's launches replayed between HIP events on the launch stream (so host launch
+    gaps between short kernels do not count)."""
     import torch
 
     import generative_recommendation_wide_amd as grw
     stream = torch.cuda.current_stream()
     loop, layers, out, ws = st["loop"], st["layers"], st["out"], st["ws"]
     d = wl.S - 1
-    calls = [(li, d) for li in range(len(layers))]
     res = {}
     for name, mask in (("shared", grw.STAGE_SHARED),
                        ("unshared_merge_fused", grw.STAGE_UNSHARED | grw.STAGE_MERGE),
                        ("unshared", grw.STAGE_UNSHARED), ("merge", grw.STAGE_MERGE)):
-        it = iter(range(10 ** 9))
-
         def fn(mask=mask):
-            li, dd = calls[next(it) % len(calls)]
-            L = layers[li]
-            grw.beam_attn_decode_stages(ws, L["q"][dd], L["k_s"], L["v_s"], L["k_scale"], L["v_scale"],
-                                        L["k_u"], L["v_u"], loop.parents, dd, out, mask)
-        res[name] = time_stage(fn, reps * len(calls), stream)
+            for L in layers:
+                grw.beam_attn_decode_stages(ws, L["q"][d], L["k_s"], L["v_s"], L["k_scale"], L["v_scale"],
+                                            L["k_u"], L["v_u"], loop.parents, d, out, mask)
+        res[name] = time_graph(fn, reps, stream) / len(layers)
 
     def sel_all():
         ws.beams_init(loop.scores[0], loop.nodes[0])
         for dd in range(wl.S):
             loop.select_step(dd, st["lps"][dd])
-    res["select_loop_3steps"] = time_stage(sel_all, reps, stream)
+    res["select_loop_3steps"] = time_graph(sel_all, reps, stream)
     return res
 
 
@@ -433,15 +467,18 @@ def batching_bench(seed, dev, budget=4096, max_requests=128):
             "same_results_both_packings": bool(same), "device_flags": flags}
 
 
-def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
+def select_roofline(seed, dev, reps, temperature=None, raw_logits=False, warm=True):
     """beam_select on the unconstrained wide-pool workload (4 requests, W = K = 512, 8192 codes,
     262144-entry pools): device time of one call with every beam live (the third decode step,
     beams from two real selections), against the HBM time of its algorithmic bytes: every
-    beam's log-probability row, the beam scores, and the four output arrays.  With a
-    temperature, beam_select_gumbel with standard Gumbel noise rows (one more row per beam
-    in the algorithmic bytes).  With raw_logits, beam_select_logits on the raw logit rows (the
-    log-softmax fused in; the same algorithmic bytes), and beside it the time of torch's
-    float32 log_softmax followed by beam_select."""
+    beam's log-probability row, the beam scores, and the four output arrays.  Timed cold:
+    a HIP graph of `reps` calls that rotate over N_COLD_SETS distinct row sets (512 MiB in
+    all, more than the 256 MB last-level cache, so every call reads its rows from HBM); and
+    warm: the same number of calls on one 64 MiB set.  With a temperature, beam_select_gumbel
+    with standard Gumbel noise rows (one more row per beam in the algorithmic bytes).  With
+    raw_logits, beam_select_logits on the raw logit rows (the log-softmax fused in; the same
+    algorithmic bytes), and beside it the time of torch's float32 log_softmax followed by
+    beam_select.  warm=False (counter runs) makes only cold calls."""
     import torch
 
     import generative_recommendation_wide_amd as grw
@@ -450,20 +487,19 @@ def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
     W, K, P = request_shapes(wl, seed)
     sumW, C = int(W.sum()), wl.C
     g = torch.Generator(device=dev).manual_seed(seed + 1)
-    lps = []
-    for _ in range(3):
+
+    def rows():
         x = torch.randn(sumW, C, generator=g, device=dev, dtype=torch.float64) * wl.logit_sigma
-        if raw_logits:
-            lps.append(x.to(torch.float32))
-        else:
-            lps.append(torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0))
-        del x
-    noise = [None] * 3
-    if temperature is not None:
-        for i in range(3):
-            u = torch.rand(sumW, C, generator=g, device=dev, dtype=torch.float64).clamp_(1e-300, 1.0 - 1e-16)
-            noise[i] = (-torch.log(-torch.log(u))).to(torch.float32)
-            del u
+        return x.to(torch.float32) if raw_logits else torch.log_softmax(x, dim=-1).to(torch.float32).clamp_max_(0.0)
+
+    def gumbel():
+        if temperature is None:
+            return None
+        u = torch.rand(sumW, C, generator=g, device=dev, dtype=torch.float64).clamp_(1e-300, 1.0 - 1e-16)
+        return (-torch.log(-torch.log(u))).to(torch.float32)
+
+    lps = [rows() for _ in range(2)]
+    noise = [gumbel() for _ in range(2)]
     ws = grw.Workspace(max_requests=len(W), max_total_beams=sumW, max_W=int(W.max()), max_K=int(K.max()),
                        max_C=C, max_S=wl.S, max_P=int(P.max()), Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                        q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype)
@@ -473,71 +509,200 @@ def select_roofline(seed, dev, reps, temperature=None, raw_logits=False):
     loop.select_step(0, lps[0], noise=noise[0], temperature=temperature or 0.0, raw_logits=raw_logits)
     loop.select_step(1, lps[1], noise=noise[1], temperature=temperature or 0.0, raw_logits=raw_logits)
     sc, nd = loop.scores[0].clone(), loop.nodes[0].clone()     # step-2 input beams
+    del lps, noise
+    sets = [(rows(), gumbel()) for _ in range(N_COLD_SETS)]    # the step-2 rows: N_COLD_SETS draws
     live = int((sc > float("-inf")).sum())
     tok, par = torch.empty(sumW, dtype=torch.int32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
     osc, ond = torch.empty(sumW, dtype=torch.float32, device=dev), torch.empty(sumW, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     Wm, Km = int(W.max()), int(K.max())
 
-    def fn():
+    def call(i):
+        x, gn = sets[i % N_COLD_SETS]
         if raw_logits:
-            grw.beam_select_logits(ws, lps[2], noise[2], temperature or 0.0, sc, nd, None, None, 0, Wm, Km, C, tok,
-                                   par, osc, ond)
+            grw.beam_select_logits(ws, x, gn, temperature or 0.0, sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
         elif temperature is None:
-            grw.beam_select(ws, lps[2], sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+            grw.beam_select(ws, x, sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
         else:
-            grw.beam_select_gumbel(ws, lps[2], noise[2], temperature, sc, nd, None, None, 0, Wm, Km, C, tok, par,
-                                   osc, ond)
-    ms_eager = time_stage(fn, reps, stream)
-    ref = (tok.clone(), par.clone(), osc.clone())
-    tok.fill_(-7)
-    # device time without host launch overhead: replay a captured graph of `reps` calls
-    # (the select kernels record no memset nodes)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(reps):
-            fn()
-    graph.replay()
-    torch.cuda.synchronize()
-    cur = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(cur)
-    for _ in range(3):
+            grw.beam_select_gumbel(ws, x, gn, temperature, sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
+
+    ms_eager = time_stage(lambda: call(0), reps, stream) if warm else float("nan")
+    refs = []
+    for i in range(N_COLD_SETS):
+        call(i)
+        torch.cuda.synchronize()
+        refs.append((tok.clone(), par.clone(), osc.clone()))
+    pools = [ws.pool_size(r) for r in range(len(W))]   # after the last set's call
+
+    def graph_ms(which):
+        """Device time per call of a captured graph of `reps` calls on sets which(i) (the select
+        kernels record no memset nodes), and whether its last call's outputs equal the eager
+        ones."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                call(which(i))
         graph.replay()
-    e1.record(cur)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (3 * reps)
-    del graph
-    same = bool(torch.equal(tok, ref[0]) and torch.equal(par, ref[1]) and
-                torch.equal(osc.view(torch.int32), ref[2].view(torch.int32)))
+        torch.cuda.synchronize()
+        tok.fill_(-7)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ref = refs[which(reps - 1) % N_COLD_SETS]
+        same = bool(torch.equal(tok, ref[0]) and torch.equal(par, ref[1]) and
+                    torch.equal(osc.view(torch.int32), ref[2].view(torch.int32)))
+        del graph
+        return e0.elapsed_time(e1) / (3 * reps), same
+
+    ms_cold, same_cold = graph_ms(lambda i: i)
+    ms_warm, same_warm = graph_ms(lambda i: 0) if warm else (float("nan"), True)
     unfused = None
     if raw_logits and temperature is None:
-        lp_buf = torch.empty_like(lps[2])
+        lp_buf = torch.empty_like(sets[0][0])
 
         def fn2():
-            torch.log_softmax(lps[2], dim=-1, out=lp_buf)
+            torch.log_softmax(sets[0][0], dim=-1, out=lp_buf)
             grw.beam_select(ws, lp_buf, sc, nd, None, None, 0, Wm, Km, C, tok, par, osc, ond)
         unfused = time_stage(fn2, reps, stream) * 1e3
-    pools = [ws.pool_size(r) for r in range(len(W))]
     bytes_ = sumW * C * 4.0 * (1 if temperature is None else 2) + sumW * 4.0 + sumW * 16.0
-    t = ms / 1e3
+    t = ms_cold / 1e3
     achieved = bytes_ / t / 1e9
+    traffic = read_traffic("select") if temperature is None and not raw_logits else None
     ws.close()
+    del sets
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "workload": "wide512u",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "workload": "wide512u",
             "live_beams": live, "bytes_per_call": bytes_, "avg_call_us": round(t * 1e6, 2),
-            "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same,
-            "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]), "timing": f"HIP graph of {reps} calls, replayed 3 times",
+            "warm_call_us": round(ms_warm * 1e3, 2), "warm_frac": round(bytes_ / (ms_warm / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "eager_call_us": round(ms_eager * 1e3, 2), "graph_matches_eager": same_cold and same_warm,
+            "pool_after_pruning": pools, "pool_unpruned": int(W[0]) * int(K[0]),
+            "timing": (f"HIP graph of {reps} calls replayed 3 times; cold: the calls rotate over {N_COLD_SETS} "
+                       f"distinct 64 MiB row sets ({N_COLD_SETS * 64} MiB); warm: one set"),
             "kernels": "select_pilot_beam_kernel + select_final_kernel",
             "entry_point": ("beam_select_logits" if raw_logits else "beam_select_gumbel" if temperature is not None
                             else "beam_select") + ("" if temperature is None else f" (temperature {temperature})"),
             "unfused_log_softmax_then_select_us": None if unfused is None else round(unfused, 2)}
 
 
+def measured_ceilings(dev):
+    """Achievable ceilings measured on this GPU beside the spec peaks: a 1 GiB device-to-device
+    copy (bytes read + written per second) and a hipBLASLt bf16 GEMM of 8192^3 through
+    torch.matmul (a plain library GEMM, measurement only)."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * 4 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * m ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del x, y, z
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "bf16_gemm_TFLOPs": round(gemm_tf, 1), "bf16_gemm_frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+            "how": "1 GiB torch copy_ (2 x bytes / time), 10 reps; torch.matmul bf16 8192^3 (hipBLASLt), 10 reps"}
+
+
+def unshared_roofline(wl, st, t_ms):
+    """The fused unshared + merge kernel at the last depth against HBM: algorithmic bytes from
+    the loop's actual parent pointers (queries of live slots, the distinct decode-token rows
+    reachable from them, the parent pointers on the walks, the shared partials, the outputs)
+    over the kernel's measured time per launch."""
+    import numpy as np
+    par = st["loop"].parents.cpu().numpy()
+    W, ws = st["W"], st["ws"]
+    d = wl.S - 1
+    kvb = {"bf16": 2, "fp8": 1, "f32": 4}[wl.kv_dtype]
+    qb = 2 if wl.q_dtype == "bf16" else 4
+    boff = np.concatenate([[0], np.cumsum(W)[:-1]]).astype(int)
+    live = nodes = walk_ptrs = 0
+    part = 0.0
+    for r, w in enumerate(W):
+        p = par[:, boff[r]:boff[r] + int(w)]
+        cur = np.nonzero(p[d] >= 0)[0]
+        live += cur.size
+        part += ws.splits(r) * cur.size * wl.Hq * (wl.D + 1) * 4.0
+        for e in range(d, -1, -1):
+            cur = np.unique(cur)
+            nodes += cur.size
+            if e > 0:
+                walk_ptrs += cur.size
+                cur = p[e][cur]
+                cur = cur[cur >= 0]
+    sumW = int(W.sum())
+    bytes_ = (live * wl.Hq * wl.D * qb + nodes * 2.0 * wl.Hkv * wl.D * kvb + (sumW + walk_ptrs) * 4.0 + part
+              + sumW * wl.Hq * wl.D * 4.0)
+    t = t_ms / 1e3
+    return {"bound": "hbm", "achieved": round(bytes_ / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(bytes_ / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "attn_unshared_kernel (merge fused)", "depth": d, "live_slots": live,
+            "distinct_decode_rows": nodes, "bytes_per_launch": bytes_, "avg_launch_us": round(t * 1e6, 2)}
+
+
+def select_loop_roofline(wl, st, t_ms):
+    """The decode loop's selections (every step, every request, on the catalog trie) against
+    HBM: algorithmic bytes are the 128-byte lines of each live beam's log-probability row that
+    hold its trie children (all lines when unconstrained), the CSR codes of those rows, the
+    beam state and the outputs; over the measured time of the S-step selection loop."""
+    import numpy as np
+    import torch
+    loop, ws, lps = st["loop"], st["ws"], st["lps"]
+    trie = st.get("trie_host")
+    sumW = int(st["W"].sum())
+    ws.beams_init(loop.scores[0], loop.nodes[0])
+    lines = codes = 0
+    for d in range(wl.S):
+        sc = loop.scores[d % 2].cpu().numpy()
+        nd = loop.nodes[d % 2].cpu().numpy()
+        for b in np.nonzero(np.isfinite(sc))[0]:
+            if trie is None:
+                lines += (wl.C * 4 + 127) // 128
+            else:
+                row = trie["code"][trie["row_ptr"][nd[b]]:trie["row_ptr"][nd[b] + 1]]
+                lines += np.unique(row // 32).size
+                codes += row.size
+        loop.select_step(d, lps[d])
+    torch.cuda.synchronize()
+    bytes_ = lines * 128.0 + codes * 4.0 + wl.S * sumW * (8.0 + 16.0)
+    t = t_ms / 1e3
+    return {"bound": "hbm", "achieved": round(bytes_ / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(bytes_ / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+            "what": f"{wl.S}-step selection loop of the decode loop ({wl.name}, catalog trie)",
+            "lines_128B": int(lines), "csr_codes": int(codes), "bytes_per_loop": bytes_,
+            "loop_us": round(t * 1e6, 2)}
+
+
 # ----------------------------------------------------------------------------------------
 # CPU oracle baseline on a bounded sample of the same workload
 # ----------------------------------------------------------------------------------------
+def oracle_cores() -> int:
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(wl, seed):
+    """The oracle on this host's cores (BLAS at one thread; the oracle's per-beam loops on a
+    thread pool of one thread per core) on a bounded sample of the workload: every request's
+    selection over all S steps, and the attention of request 0's slots at the last depth on one
+    layer; scaled to every request, beam and layer of a decode step."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -545,55 +710,114 @@ def cpu_baseline(wl, seed):
     from oracle.select import catalog_prefix_sets, initial_beams, oracle_select
     from synth import attention_layer, catalog_items, logprob_rows, random_parents, request_shapes
 
+    n = oracle_cores()
     W, K, P = request_shapes(wl, seed)
-    R, W0, K0 = len(W), int(W[0]), int(K[0])
+    R = len(W)
     items = catalog_items(wl, seed)
     psets = catalog_prefix_sets(items, wl.C) if items is not None else None
-    # bounded sample: request 0 cut to its first 512 beam slots and 3 steps, scaled linearly
-    Ws, Ss = min(W0, 512), min(wl.S, 3)
+    boff = np.concatenate([[0], np.cumsum(W)[:-1]]).astype(int)
     with threadpool_limits(limits=1):
-        # selection: request 0 (sampled), its own parents, timed
         t_sel = 0.0
-        scores, prefixes = initial_beams(Ws)
-        for d in range(Ss):
-            lp = logprob_rows(wl, d, seed, rows=np.arange(Ws))
-            t0 = time.perf_counter()
-            res = oracle_select(lp, scores, prefixes, d, K0, Ws, wl.C, psets)
-            t_sel += time.perf_counter() - t0
-            scores, prefixes = res["scores"], res["prefixes"]
-        t_sel *= (W0 / Ws) * (wl.S / Ss)
-        # attention: a few beams of request 0, layer 0, deepest step
+        lps = [logprob_rows(wl, d, seed) for d in range(wl.S)]
+        for r in range(R):
+            scores, prefixes = initial_beams(int(W[r]))
+            for d in range(wl.S):
+                lp = lps[d][boff[r]:boff[r] + int(W[r])]
+                t0 = time.perf_counter()
+                res = oracle_select(lp, scores, prefixes, d, int(K[r]), int(W[r]), wl.C, psets, threads=n)
+                t_sel += time.perf_counter() - t0
+                scores, prefixes = res["scores"], res["prefixes"]
+        del lps
         layer = attention_layer(wl, 0, seed, requests=[0])
         par = random_parents(wl, seed)
-        nb = min(6, W0)
+        W0 = int(W[0])
+        nb = min(W0, 512)
         d = wl.S - 1
         t0 = time.perf_counter()
         oracle_attention(layer["q"][d][:W0], layer["k_s"][0], layer["v_s"][0], layer["k_u"][:, :W0],
                          layer["v_u"][:, :W0], par[:, :W0], d, q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
-                         k_scale=layer["k_scale"], v_scale=layer["v_scale"], beams=range(nb))
+                         k_scale=layer["k_scale"], v_scale=layer["v_scale"], beams=range(nb), threads=n)
         t_attn_beam = (time.perf_counter() - t0) / nb
     sumW = int(W.sum())
-    t_step = R * t_sel / wl.S + sumW * wl.layers * t_attn_beam
-    return {"value": 1.0 / t_step, "unit": "beam decode steps/s", "cores": 1, "kind": "oracle",
-            "sample": (f"oracle_select on request 0 ({Ws} of its {W0} slots, {Ss} of {wl.S} steps, scaled "
-                       f"to all: {t_sel:.2f} s) and "
-                       f"oracle_attention on {nb} beams of request 0, layer 0, depth {d} "
-                       f"({t_attn_beam * 1e3:.0f} ms/beam); scaled to {R} requests x {sumW} beams "
-                       f"x {wl.layers} layers per decode step; BLAS limited to 1 thread")}
+    t_step = t_sel / wl.S + sumW * wl.layers * t_attn_beam
+    return {"value": 1.0 / t_step, "unit": "beam decode steps/s", "cores": n, "kind": "oracle",
+            "sample": (f"oracle_select on all {R} requests over all {wl.S} steps ({t_sel:.2f} s) and "
+                       f"oracle_attention on {nb} slots of request 0, layer 0, depth {d} "
+                       f"({t_attn_beam * 1e3:.2f} ms per slot); scaled to {sumW} slots x {wl.layers} layers per "
+                       f"decode step; {n} threads (per-beam thread pool), BLAS at 1 thread")}
 
 
-def read_traffic():
-    if not os.path.exists(TRAFFIC_FILE):
+def cpu_full(name, seed):
+    """The oracle on a whole small workload, in full: every request, every decode step (the
+    selection, then every layer's attention of every slot at that depth with the parents the
+    selection chose), on this host's cores.  Returns decode steps per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.attention import oracle_attention
+    from oracle.select import catalog_prefix_sets, initial_beams, oracle_select
+    from synth import attention_layer, catalog_items, logprob_rows, request_shapes, workload
+
+    wl = workload(name)
+    n = oracle_cores()
+    W, K, P = request_shapes(wl, seed)
+    items = catalog_items(wl, seed)
+    psets = catalog_prefix_sets(items, wl.C) if items is not None else None
+    boff = np.concatenate([[0], np.cumsum(W)[:-1]]).astype(int)
+    lps = [logprob_rows(wl, d, seed) for d in range(wl.S)]
+    layers = [attention_layer(wl, li, seed) for li in range(wl.layers)]
+    total = 0.0
+    with threadpool_limits(limits=1):
+        for r in range(len(W)):
+            a, w = boff[r], int(W[r])
+            scores, prefixes = initial_beams(w)
+            par = np.full((wl.S, w), -1, np.int32)
+            for d in range(wl.S):
+                t0 = time.perf_counter()
+                res = oracle_select(lps[d][a:a + w], scores, prefixes, d, int(K[r]), w, wl.C, psets, threads=n)
+                scores, prefixes = res["scores"], res["prefixes"]
+                par[d] = res["parents"]
+                for L in layers:
+                    oracle_attention(L["q"][d][a:a + w], L["k_s"][r], L["v_s"][r], L["k_u"][:, a:a + w],
+                                     L["v_u"][:, a:a + w], par, d, q_dtype=wl.q_dtype, kv_dtype=wl.kv_dtype,
+                                     k_scale=L["k_scale"], v_scale=L["v_scale"], threads=n)
+                total += time.perf_counter() - t0
+    return {"workload": name, "value": round(wl.S / total, 4), "unit": "beam decode steps/s", "cores": n,
+            "seconds": round(total, 2), "requests": len(W), "slots": int(W.sum()), "steps": wl.S,
+            "layers": wl.layers}
+
+
+def _read_record(path, sources):
+    """key = value lines of a counter record, or None when it is missing or was taken from
+    other kernel sources."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != kernel_source_sha():
+    if kv.get("source_sha") != kernel_source_sha(sources):
+        return None
+    return kv
+
+
+def read_traffic(target="shared"):
+    path, _, sources, _, _ = TRAFFIC[target]
+    kv = _read_record(path, sources)
+    try:
+        return None if kv is None else float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma():
+    kv = _read_record(MFMA_FILE, KERNEL_SOURCES)
+    if kv is None:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return {k: float(kv[k]) for k in ("mfma_busy", "coexec_of_mfma_busy", "valu_per_mfma", "lds_bank_conflict_cycles",
+                                          "mfma_insts")}
     except (KeyError, ValueError):
         return None
 
@@ -651,50 +875,126 @@ def summarize(args):
     print(text)
 
 
-def write_traffic(args):
-    """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs (FETCH_SIZE,
-    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for the
-    calibration copy (the largest copyBuffer dispatch, of --calib-copy-mib MiB)."""
+def _counter_rows(d):
     import csv
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return list(csv.DictReader(open(f[0])))
+
+
+def write_traffic(args):
+    """HBM bytes per launch (per call for the selection: its kernels' dispatches summed) from
+    two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the calibration copy (the largest copyBuffer dispatch, of
+    --calib-copy-mib MiB)."""
     fetch_dir, write_dir = args.traffic
+    path, kernels, sources, what, flags = TRAFFIC[args.traffic_target]
     calib_kib = args.calib_copy_mib * 1024.0
 
     def per_dispatch(d, counter):
-        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
-        dom, copies = [], []
-        for r in csv.DictReader(open(f)):
+        per_k = {k: [] for k in kernels}
+        copies = []
+        for r in _counter_rows(d):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if DOMINANT in r["Kernel_Name"]:
-                dom.append(v)
-            elif "copyBuffer" in r["Kernel_Name"]:
+            for k in kernels:
+                if k in r["Kernel_Name"]:
+                    per_k[k].append(v)
+            if "copyBuffer" in r["Kernel_Name"]:
                 copies.append(v)
-        return sum(dom) / len(dom), max(copies)
+        # the median dispatch: the selection's first step (one live beam per request) and any
+        # other odd dispatch do not move it
+        return {k: sorted(v)[len(v) // 2] for k, v in per_k.items()}, max(copies)
 
     fk, fcal = per_dispatch(fetch_dir, "FETCH_SIZE")
     wk, wcal = per_dispatch(write_dir, "WRITE_SIZE")
     ff, wf = calib_kib / fcal, calib_kib / wcal
-    total = (fk * ff + wk * wf) * 1024.0
+    total = (sum(fk.values()) * ff + sum(wk.values()) * wf) * 1024.0
     lines = [
-        f"# HBM traffic of {DOMINANT} per launch (wide512: one layer, 4 requests, W=K=512, P=4096)",
+        f"# HBM traffic of {' + '.join(kernels)} per launch ({what})",
         "# Commands (repo root on the GPU box, TMPDIR=/tmp), one counter per run:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d $GRAFT_REPO_ROOT/gpurun_out/pmc_fetch -o run --output-format csv -- "
-        f"python $GRAFT_REPO_ROOT/bench.py --steps 1 --warmup 1 --stage-reps 0 --no-cpu-baseline --calib-copy-mib {args.calib_copy_mib}",
-        "#   (same with --pmc WRITE_SIZE -d .../pmc_write)",
-        f"#   python bench.py --traffic gpurun_out/pmc_fetch gpurun_out/pmc_write --calib-copy-mib {args.calib_copy_mib}",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
+        f"python3 bench.py {flags} --no-cpu-baseline --counter-run --calib-copy-mib {args.calib_copy_mib}",
+        "#   (same with --pmc WRITE_SIZE -d gpurun_out/pmc_write)",
+        f"#   python bench.py --traffic gpurun_out/pmc_fetch gpurun_out/pmc_write --traffic-target {args.traffic_target} "
+        f"--calib-copy-mib {args.calib_copy_mib}",
         f"# calibration: a {args.calib_copy_mib} MiB device copy reads FETCH_SIZE={fcal:.1f} KiB and WRITE_SIZE={wcal:.1f} KiB,",
         f"# so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f}.",
-        f"fetch_kib_raw={fk:.1f}",
-        f"write_kib_raw={wk:.1f}",
+    ]
+    for k in kernels:
+        lines.append(f"# {k}: FETCH_SIZE {fk[k]:.1f} KiB, WRITE_SIZE {wk[k]:.1f} KiB per dispatch (raw, median)")
+    lines += [
+        f"fetch_kib_raw={sum(fk.values()):.1f}",
+        f"write_kib_raw={sum(wk.values()):.1f}",
         f"fetch_scale={ff:.4f}",
         f"write_scale={wf:.4f}",
         f"hbm_bytes_per_launch={total:.0f}",
-        f"source_sha={kernel_source_sha()}",
+        f"source_sha={kernel_source_sha(sources)}",
     ]
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def write_mfma(args):
+    """MFMA utilisation of the dominant kernel from two rocprofv3 --pmc runs (per dispatch):
+    run 1 SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE,
+    run 2 SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES GRBM_GUI_ACTIVE.  MFMA busy = busy
+    cycles (counted per SIMD, summed over the chip's SIMDs) / (SIMDs x active GPU cycles of one
+    XCD; GRBM_GUI_ACTIVE is reported summed over the 8 XCDs)."""
+    vals = {}
+    for d in args.mfma:
+        acc = {}
+        for r in _counter_rows(d):
+            if DOMINANT not in r["Kernel_Name"]:
+                continue
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, v in acc.items():
+            vals.setdefault(k, []).extend(v)
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    xcd_cycles = avg["GRBM_GUI_ACTIVE"] / N_XCDS
+    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMDS * xcd_cycles)
+    lines = [
+        f"# MFMA counters of {DOMINANT} per dispatch (wide512: one layer, 4 requests, W=K=512, P=4096)",
+        "# Commands (repo root on the GPU box, TMPDIR=/tmp):",
+        "#   rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE "
+        "-d gpurun_out/pmc_mfma1 -o run --output-format csv -- python3 bench.py --steps 1 --warmup 1 --stage-reps 0 "
+        "--no-cpu-baseline --counter-run",
+        "#   rocprofv3 --pmc SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d gpurun_out/pmc_mfma2 ...",
+        "#   python bench.py --mfma gpurun_out/pmc_mfma1 gpurun_out/pmc_mfma2",
+        "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); coexec_of_mfma_busy =",
+        "# SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; valu_per_mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA",
+    ]
+    for k in sorted(avg):
+        lines.append(f"# {k}: {avg[k]:.1f}")
+    lines += [
+        f"# active cycles per XCD: {xcd_cycles:.0f} ({xcd_cycles / 2.4e3:.1f} us at 2.4 GHz)",
+        f"mfma_insts={avg['SQ_INSTS_MFMA']:.0f}",
+        f"mfma_busy={busy:.4f}",
+        f"coexec_of_mfma_busy={avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}",
+        f"valu_per_mfma={avg.get('SQ_INSTS_VALU', float('nan')) / avg['SQ_INSTS_MFMA']:.3f}",
+        f"lds_bank_conflict_cycles={avg.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f}",
+        f"source_sha={kernel_source_sha(KERNEL_SOURCES)}",
+    ]
+    with open(MFMA_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def calib_copy(args, dev):
+    """One device copy of --calib-copy-mib MiB (the counters' calibration dispatch)."""
+    if not args.calib_copy_mib:
+        return
+    import torch
+    n = args.calib_copy_mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 # ----------------------------------------------------------------------------------------
@@ -723,6 +1023,14 @@ def main():
                     help="time the first-step fan-out against the plain first step on the ultra-wide shape")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--traffic-target", default="shared", choices=sorted(TRAFFIC))
+    ap.add_argument("--mfma", nargs="+", default=None, metavar="PMC_DIR",
+                    help="write the dominant kernel's MFMA counter record from rocprofv3 --pmc output")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="short run for rocprofv3 counters: no graph replays, no two-stream timing, cold selection "
+                         "calls only")
+    ap.add_argument("--no-cpu-full", action="store_true",
+                    help="skip the oracle's full runs of the two small workloads")
     ap.add_argument("--summary-out", default=None)
     ap.add_argument("--summary-header", default="")
     args = ap.parse_args()
@@ -731,6 +1039,9 @@ def main():
         return 0
     if args.traffic:
         write_traffic(args)
+        return 0
+    if args.mfma:
+        write_mfma(args)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -755,8 +1066,11 @@ def main():
         print(json.dumps(batching_bench(args.seed, dev)), flush=True)
         return 0
     if args.select_only:
-        print(json.dumps(select_roofline(args.seed, dev, 20, temperature=args.select_temperature,
-                                         raw_logits=args.select_logits)), flush=True)
+        print(json.dumps(select_roofline(args.seed, dev, 16 * max(1, args.stage_reps),
+                                         temperature=args.select_temperature, raw_logits=args.select_logits,
+                                         warm=not args.counter_run)),
+              flush=True)
+        calib_copy(args, dev)
         return 0
     log(f"[bench] setting up {wl.name} ...")
     t_setup = time.perf_counter()
@@ -781,20 +1095,21 @@ def main():
     log(f"[bench] timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {ev * 1e3:.2f} ms")
     decode_steps = wl.S * args.steps
     value = decode_steps / wall
-    # the same loop captured as one HIP graph and replayed (no host work between kernels)
-    graph = loop.capture(lps, layers, out)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_wall = time.perf_counter() - t0
-    del graph
-    graph_value = decode_steps / graph_wall
-    log(f"[bench] graph replay of {args.steps} steps: wall {graph_wall * 1e3:.2f} ms")
-
-    overlap = overlap_timings(wl, st, args.steps)
-    log(f"[bench] two-stream attention: {overlap}")
+    graph_value = overlap = None
+    if not args.counter_run:
+        # the same loop captured as one HIP graph and replayed (no host work between kernels)
+        graph = loop.capture(lps, layers, out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        del graph
+        graph_value = round(decode_steps / graph_wall, 2)
+        log(f"[bench] graph replay of {args.steps} steps: wall {graph_wall * 1e3:.2f} ms")
+        overlap = overlap_timings(wl, st, args.steps)
+        log(f"[bench] two-stream attention: {overlap}")
     if args.stage_reps > 0:
         stages = stage_timings(wl, st, args.stage_reps)
     else:
@@ -805,32 +1120,43 @@ def main():
     t_shared = stages["shared"] / 1e3
     achieved = flops / t_shared / 1e12
     traffic = read_traffic()
+    mfma = read_mfma()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "mfma_busy": None if mfma is None else mfma["mfma_busy"],
                 "kernel": DOMINANT, "flops_per_launch": flops, "avg_launch_us": round(t_shared * 1e6, 2),
                 "algorithmic_bytes_per_launch": bytes_,
-                "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1)}
-    sel_roof = sel_gumbel = sel_logits = None
+                "algorithmic_hbm_GBs": round(bytes_ / t_shared / 1e9, 1),
+                "counters": mfma}
+    sel_roof = sel_gumbel = sel_logits = uns_roof = sel_loop_roof = ceilings = None
     if args.stage_reps > 0:
-        sel_roof = select_roofline(args.seed, dev, 20 * args.stage_reps)
+        uns_roof = unshared_roofline(wl, st, stages["unshared_merge_fused"])
+        log(f"[bench] unshared + merge: {uns_roof}")
+        sel_loop_roof = select_loop_roofline(wl, st, stages["select_loop_3steps"])
+        log(f"[bench] select loop: {sel_loop_roof}")
+        ceilings = measured_ceilings(dev)
+        log(f"[bench] measured ceilings: {ceilings}")
+        if ceilings:
+            roofline["frac_of_measured_gemm"] = round(achieved / ceilings["bf16_gemm_TFLOPs"], 4)
+        sel_roof = select_roofline(args.seed, dev, 16 * args.stage_reps)
         log(f"[bench] select on wide512u: {sel_roof}")
-        sel_gumbel = select_roofline(args.seed, dev, 20 * args.stage_reps, temperature=1.0)
+        sel_gumbel = select_roofline(args.seed, dev, 16 * args.stage_reps, temperature=1.0)
         log(f"[bench] Gumbel select on wide512u: {sel_gumbel}")
-        sel_logits = select_roofline(args.seed, dev, 20 * args.stage_reps, raw_logits=True)
+        sel_logits = select_roofline(args.seed, dev, 16 * args.stage_reps, raw_logits=True)
         log(f"[bench] select from raw logits on wide512u: {sel_logits}")
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    calib_copy(args, dev)
 
-    cpu = None
+    cpu = cpu_small = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample ...")
+        log(f"[bench] timing the CPU oracle on a bounded sample ({oracle_cores()} cores) ...")
         cpu = cpu_baseline(wl, args.seed)
+        log(f"[bench] oracle: {cpu}")
+        if not args.no_cpu_full:
+            cpu_small = []
+            for name in ("tiny", "qwen06b"):
+                log(f"[bench] the oracle on all of {name} ...")
+                cpu_small.append(cpu_full(name, args.seed))
+                log(f"[bench] {cpu_small[-1]}")
     res = {
         "metric": "beam decode steps/s (attn+select) at W=K=512; achieved HBM GB/s vs peak",
         "value": round(value, 2),
@@ -850,14 +1176,18 @@ def main():
                    "decode_steps_per_bench_step": wl.S,
                    "trie": None if wl.catalog is None else f"{wl.catalog[0]} {wl.catalog[1]} items",
                    "device_flags": flags},
-        "graph_replay_value": round(graph_value, 2),
+        "graph_replay_value": graph_value,
         "two_stream_attention": overlap,
         "stages_ms_per_call": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
+        "measured_ceilings": ceilings,
+        "unshared_roofline": uns_roof,
+        "select_loop_roofline": sel_loop_roof,
         "select_roofline": sel_roof,
         "select_gumbel_roofline": sel_gumbel,
         "select_logits_roofline": sel_logits,
         "cpu_baseline": cpu,
+        "cpu_oracle_full_small_workloads": cpu_small,
     }
     print(json.dumps(res), flush=True)
     return 0
