@@ -285,8 +285,8 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, fmaxf(s0[k], s1[k]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    for (int k = 0; k < 16; ++k) mx = vmax(mx, vmax(s0[k], s1[k]));
+    mx = vmax(mx, __shfl_xor(mx, 32, 64)) * c;
     // Lazy rescale: the running max m_run only moves when some row's tile max exceeds it
     // by more than kRescale (log2 units), so p = 2^(s*c - m_run) <= 2^kRescale and the
     // O / l rescale runs on a few tiles only (wave-uniform branch).
@@ -405,26 +405,35 @@ constexpr int FLAG = ALPHA + 2 * 4 * 64 * 4;          // rescale flags [2][4] in
 constexpr int SMEM_BYTES = FLAG + 2 * 4 * 4;
 
 // Direct-to-LDS loads of one K tile (rows in k_row_key order, swizzled) and one V^T tile:
-// each wave moves 2 KB of each.
-__device__ __forceinline__ void issue_k(uint8_t* dst, const uint8_t* kb, int p, int wave, int lane) {
+// each wave moves 2 KB of each, chunks 2 wave and 2 wave + 1.  A lane's byte offsets within
+// a tile do not depend on the tile, so they are formed once (TileOffsets); per tile only the
+// tile's base address (wave-uniform) moves, and the LDS destinations are scalar.
+struct TileOffsets {
+  uint32_t k[2], v[2];
+};
+__device__ __forceinline__ TileOffsets tile_offsets(int wave, int lane, int Pp) {
+  TileOffsets t;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int blk = wave * 2 + i;
-    const int j = blk * 64 + lane;
-    const int r = j >> 4, lc = (j & 15) ^ (r & 15);
-    const uint8_t* src = kb + ((size_t)(p + lds::k_row_key(r)) * DH + lc * 8) * 2;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds::lds_void*)(dst + blk * 1024), 16, 0, 0);
+    const int j = (wave * 2 + i) * 64 + lane;
+    const int r = j >> 4, lk = (j & 15) ^ (r & 15);
+    t.k[i] = (uint32_t)((lds::k_row_key(r) * DH + lk * 8) * 2);          // < 16 KB
+    const int d = j >> 3, lv = (j & 7) ^ ((d >> 1) & 7);
+    t.v[i] = (uint32_t)(d * Pp + lv * 8) * 2u;                           // within the prompt block
   }
+  return t;
 }
-__device__ __forceinline__ void issue_v(uint8_t* dst, const uint8_t* vb, int p, int Pp, int wave, int lane) {
+__device__ __forceinline__ void issue_k(uint8_t* dst, const uint8_t* kb, int p, int wave, const TileOffsets& t) {
+  const uint8_t* base = kb + (size_t)p * (DH * 2);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = wave * 2 + i;
-    const int j = blk * 64 + lane;
-    const int d = j >> 3, lc = (j & 7) ^ ((d >> 1) & 7);
-    const uint8_t* src = vb + ((size_t)d * Pp + p + lc * 8) * 2;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds::lds_void*)(dst + blk * 1024), 16, 0, 0);
-  }
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(base + t.k[i]), (lds::lds_void*)(dst + (wave * 2 + i) * 1024), 16, 0, 0);
+}
+__device__ __forceinline__ void issue_v(uint8_t* dst, const uint8_t* vb, int p, int wave, const TileOffsets& t) {
+  const uint8_t* base = vb + (size_t)p * 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(base + t.v[i]), (lds::lds_void*)(dst + (wave * 2 + i) * 1024), 16, 0, 0);
 }
 
 // Normalised partial output and LSE of one 32-row block (rows row0 .. row0 + 31 of the
@@ -480,7 +489,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
   const ShWork wk = work[blockIdx.x];
   if (wk.r < 0) return;
   const ReqDesc rd = a.req[wk.r];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = a.g, Hq = a.Hq, h = wk.h;
   const int nrows = rd.W * g;
@@ -493,7 +503,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
   float* const alpha_s = (float*)(smem + ALPHA);
   int* const flag_s = (int*)(smem + FLAG);
 
-  issue_k(smem + KRING, kb, p0, wave, lane);
+  const TileOffsets toff = tile_offsets(wave, lane, rd.Pp);
+  issue_k(smem + KRING, kb, p0, wave, toff);
 
   if (scorer) {
     // ---------------- score wave: S^T, running max, P ----------------
@@ -520,8 +531,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
     for (int i = 0; i <= ntiles; ++i) {
       lds::wait_all_vm();
       __syncthreads();
-      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, lane);
-      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, rd.Pp, wave, lane);
+      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, toff);
+      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, wave, toff);
       if (i == ntiles) break;
       const uint8_t* st = smem + KRING + (i & 1) * TILE_BYTES;
       const int p = p0 + i * NT;
@@ -566,8 +577,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
       for (int qb = 0; qb < 2; ++qb) {
         float m = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(s[0][qb][k], s[1][qb][k]));
-        mx[qb] = fmaxf(m, __shfl_xor(m, 32, 64)) * c;
+        for (int k = 0; k < 16; ++k) m = vmax(m, vmax(s[0][qb][k], s[1][qb][k]));
+        mx[qb] = vmax(m, __shfl_xor(m, 32, 64)) * c;
       }
       // lazy rescale as in the kernels above; the product wave applies the factor to O and l
       const int bi = (i & 1) * 4 + sw;
@@ -616,8 +627,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
     for (int i = 0; i <= ntiles; ++i) {
       lds::wait_all_vm();
       __syncthreads();
-      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, lane);
-      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, rd.Pp, wave, lane);
+      if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, toff);
+      if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, wave, toff);
       if (i == 0) continue;
       const int bt = ((i - 1) & 1) * 4 + sw;
       if (flag_s[bt]) {

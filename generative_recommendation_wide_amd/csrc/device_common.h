@@ -87,6 +87,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Maximum that propagates NaN (IEEE 754-2019 maximum).  Chains of it lower to
+// v_maximum3_f32; fmaxf on MFMA results costs an extra canonicalising v_max per operand.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
