@@ -617,9 +617,64 @@ def measured_ceilings(dev):
     torch.cuda.synchronize()
     gemm_tf = 2.0 * m ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
     del x, y, z
-    return {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
-            "bf16_gemm_TFLOPs": round(gemm_tf, 1), "bf16_gemm_frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
-            "how": "1 GiB torch copy_ (2 x bytes / time), 10 reps; torch.matmul bf16 8192^3 (hipBLASLt), 10 reps"}
+    res = {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+           "bf16_gemm_TFLOPs": round(gemm_tf, 1), "bf16_gemm_frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4),
+           "how": "1 GiB torch copy_ (2 x bytes / time), 10 reps; torch.matmul bf16 8192^3 (hipBLASLt), 10 reps"}
+    res.update(mfma_ceiling(dev))
+    return res
+
+
+def mfma_ceiling(dev, launches=8, iters=20000):
+    """Dense bf16 MFMA rate of the whole chip under sustained load, from the probe in
+    libgrw_ceiling.so: one 4-wave workgroup per CU, 8 independent 32x32x16 accumulations per
+    wave, `launches` back-to-back launches (about 20 ms; the clock ramps up over the first
+    ones, so the rate is the last launch's).  Also that launch's shader clock (s_memtime
+    cycles over s_memrealtime 100 MHz ticks, median over workgroups) and the dense peak at that
+    clock (1024 flops per SIMD and cycle, 1024 SIMDs).  With every matrix pipe busy the chip
+    clocks down well below the 2.4 GHz of the spec peak; a kernel that keeps the pipes busy
+    part of the time runs at a higher clock, so its MFMA busy fraction (counters) is the
+    cycle-level measure."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "generative_recommendation_wide_amd",
+                        "libgrw_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP libraries first")
+    lib = ctypes.CDLL(path)
+    lib.grw_ceiling_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.grw_ceiling_mfma_per_round.restype = ctypes.c_int
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ts = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    if lib.grw_ceiling_mfma(blocks, iters, out.data_ptr(), ts.data_ptr(), sp) != 0:
+        raise RuntimeError("grw_ceiling_mfma failed")
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    ev[0].record(stream)
+    for j in range(launches):
+        if lib.grw_ceiling_mfma(blocks, iters, out.data_ptr(), ts.data_ptr(), sp) != 0:
+            raise RuntimeError("grw_ceiling_mfma failed")
+        ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per_round = lib.grw_ceiling_mfma_per_round()
+    mfmas_per_wave = per_round * iters
+    flops = 32768.0 * mfmas_per_wave * 4 * blocks
+    # the clock ramps up under sustained load: the rate and the clock are those of the last launch
+    tf = flops / (ev[launches - 1].elapsed_time(ev[launches]) / 1e3) / 1e12
+    t = ts.cpu().numpy().reshape(blocks, 2).astype(np.float64)
+    ghz = float(np.median(t[:, 0] / (t[:, 1] * 10.0)))
+    cyc = float(np.median(t[:, 0] / mfmas_per_wave))
+    peak_at_clock = 1024.0 * 1024 * ghz * 1e9 / 1e12
+    return {"mfma_bf16_TFLOPs": round(tf, 1), "mfma_bf16_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "mfma_cycles_per_32x32x16": round(cyc, 2), "shader_clock_GHz_under_mfma_load": round(ghz, 3),
+            "dense_bf16_peak_at_that_clock_TFLOPs": round(peak_at_clock, 1),
+            "mfma_how": (f"libgrw_ceiling.so probe: {blocks} workgroups x 4 waves, {per_round} independent "
+                         f"32x32x16 bf16 accumulations per wave, {iters} rounds, {launches} launches back to back; "
+                         "rate and clock (s_memtime cycles / s_memrealtime 100 MHz ticks) of the last launch")}
 
 
 def unshared_roofline(wl, st, t_ms):
@@ -1138,6 +1193,7 @@ def main():
         log(f"[bench] measured ceilings: {ceilings}")
         if ceilings:
             roofline["frac_of_measured_gemm"] = round(achieved / ceilings["bf16_gemm_TFLOPs"], 4)
+            roofline["frac_of_measured_mfma_rate"] = round(achieved / ceilings["mfma_bf16_TFLOPs"], 4)
         sel_roof = select_roofline(args.seed, dev, 16 * args.stage_reps)
         log(f"[bench] select on wide512u: {sel_roof}")
         sel_gumbel = select_roofline(args.seed, dev, 16 * args.stage_reps, temperature=1.0)

@@ -5,7 +5,9 @@
 (run it by path: importing the package loads the library this script builds)
 
 Every source is compiled with hipcc for gfx950 only, with packed-FP32 instruction
-selection disabled, then linked into one shared library next to this file.
+selection disabled, then linked into one shared library next to this file.  The benchmark's
+MFMA ceiling probe (csrc/ceiling.hip) goes into a library of its own, libgrw_ceiling.so, so
+that the decode library holds the decode path only.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgrw.so")
 SOURCES = ["api.hip", "attn_shared.hip", "attn_unshared.hip", "select.hip"]
+CEILING_LIB = os.path.join(HERE, "libgrw_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -55,18 +59,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link(LIB, [objs[s] for s in SOURCES])
+    _link(CEILING_LIB, [objs[s] for s in CEILING_SOURCES])
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEILING_LIB)
     return LIB
 
 

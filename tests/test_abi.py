@@ -84,3 +84,20 @@ def test_null_handles_rejected(clib):
     assert f(None, None, None, 0.0, None, None, None, None, 0, 1, 1, 1, None, None, None, None, None) == 1
     assert clib.grw_backtrack(None, None, None, 1, None, None) == 1
     assert clib.grw_ws_pool_size(None, 0, None, None) == 1
+
+
+def test_ceiling_probe_library_is_separate(clib):
+    """The benchmark's MFMA ceiling probe lives in its own library: it loads and exports its
+    launcher, and the decode library does not carry it."""
+    path = os.path.join(ROOT, "generative_recommendation_wide_amd", "libgrw_ceiling.so")
+    if not os.path.exists(path):
+        import __graft_entry__
+        __graft_entry__._build_module().build()
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "grw_ceiling_mfma")
+    lib.grw_ceiling_mfma_per_round.restype = ctypes.c_int
+    assert lib.grw_ceiling_mfma_per_round() == 8
+    # invalid arguments are rejected on the host, before any launch
+    lib.grw_ceiling_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.grw_ceiling_mfma(0, 10, None, None, None) == -1
+    assert not hasattr(clib, "grw_ceiling_mfma")
