@@ -147,6 +147,20 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return r;
 }
 
+// Maximum of the 32 scores a lane holds for one row (16 of each of two key blocks) as a tree
+// of three-input maxima: 18 instructions, 4 dependent steps (a running chain takes 16 steps).
+__device__ __forceinline__ float max32(const floatx16& x, const floatx16& y) {
+  float t[11];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) t[j] = vmax(vmax(x[3 * j], x[3 * j + 1]), x[3 * j + 2]);
+#pragma unroll
+  for (int j = 0; j < 5; ++j) t[5 + j] = vmax(vmax(y[3 * j], y[3 * j + 1]), y[3 * j + 2]);
+  t[10] = vmax(x[15], y[15]);
+  const float u0 = vmax(vmax(t[0], t[1]), t[2]), u1 = vmax(vmax(t[3], t[4]), t[5]);
+  const float u2 = vmax(vmax(t[6], t[7]), t[8]), u3 = vmax(t[9], t[10]);
+  return vmax(vmax(vmax(u0, u1), u2), u3);
+}
+
 // Store a wave's 32 rows of normalised partial output and their LSE.  The partial output
 // goes out through LDS so that every store instruction writes whole rows (512 B per query
 // row): written straight from the MFMA layout, each instruction would put 32-byte pieces of
@@ -283,9 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
         if (key + 32 >= p1) s1[k] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) mx = vmax(mx, vmax(s0[k], s1[k]));
+    float mx = max32(s0, s1);
     mx = vmax(mx, __shfl_xor(mx, 32, 64)) * c;
     // Lazy rescale: the running max m_run only moves when some row's tile max exceeds it
     // by more than kRescale (log2 units), so p = 2^(s*c - m_run) <= 2^kRescale and the
@@ -575,9 +587,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
       float mx[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) m = vmax(m, vmax(s[0][qb][k], s[1][qb][k]));
+        const float m = max32(s[0][qb], s[1][qb]);
         mx[qb] = vmax(m, __shfl_xor(m, 32, 64)) * c;
       }
       // lazy rescale as in the kernels above; the product wave applies the factor to O and l
