@@ -520,6 +520,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
 
   if (scorer) {
     // ---------------- score wave: S^T, running max, P ----------------
+    // The score products deliver the exponent arguments x = c s - m (log2 units) directly:
+    // Q is held pre-scaled by c = log2(e) / sqrt(D) (one bf16 rounding of c q), and a ninth
+    // k-step adds -m to every row, its K fragment holding ones in dimensions 0 and 1 and its Q
+    // fragment the row's -m_hi, -m_lo.  The running max m is kept as m_hi + m_lo (two bf16
+    // values, the sum exact in float), so the m the products subtract is the m of the LSE.
     const float c = rsqrtf((float)DH) * kLog2e;
     bf16x8 qf[2][DH / 16];
 #pragma unroll
@@ -532,14 +537,32 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
 #pragma unroll
       for (int ks = 0; ks < DH / 16; ++ks) {
         if (ok) {
-          qf[qb][ks] = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
+          const bf16x8 q8 = *(const bf16x8*)(qrow + ks * 16 + hi * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (__bf16)((float)q8[e] * c);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (__bf16)0.0f;
         }
       }
     }
-    float m_run[2] = {-INFINITY, -INFINITY};
+    bf16x8 kone, qm[2];   // the extra k-step's K fragment, and its Q fragment per row block
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kone[e] = (__bf16)((hi == 0 && e < 2) ? 1.0f : 0.0f);
+      qm[0][e] = qm[1][e] = (__bf16)0.0f;
+    }
+    // sets row block qb's subtracted max to (about) m; returns the value subtracted
+    auto set_m = [&](int qb, float m) -> float {
+      const __bf16 mh = (__bf16)m;
+      const __bf16 ml = (__bf16)(m - (float)mh);
+      if (hi == 0) {
+        qm[qb][0] = (__bf16)(-(float)mh);
+        qm[qb][1] = (__bf16)(-(float)ml);
+      }
+      return (float)mh + (float)ml;
+    };
+    float m_run[2] = {0.0f, 0.0f};
     for (int i = 0; i <= ntiles; ++i) {
       lds::wait_all_vm();
       __syncthreads();
@@ -549,11 +572,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
       const uint8_t* st = smem + KRING + (i & 1) * TILE_BYTES;
       const int p = p0 + i * NT;
       floatx16 s[2][2];   // [key block][row block]
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb2][qb] = floatx16{};
-      __builtin_amdgcn_s_setprio(2);
+        for (int qb = 0; qb < 2; ++qb) s[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qm[qb], floatx16{}, 0, 0, 0);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 kf[2][4];
@@ -584,22 +607,29 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
           }
         }
       }
-      float mx[2];
+      float mx[2];   // the row's largest x in this tile
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m = max32(s[0][qb], s[1][qb]);
-        mx[qb] = vmax(m, __shfl_xor(m, 32, 64)) * c;
+        mx[qb] = vmax(m, __shfl_xor(m, 32, 64));
       }
-      // lazy rescale as in the kernels above; the product wave applies the factor to O and l
+      // Lazy rescale as in the kernels above: m moves when some row's x exceeds kRescale (on
+      // the first tile, to the tile max); then x drops by the shift and the product wave
+      // scales O and l by 2^-shift.
       const int bi = (i & 1) * 4 + sw;
-      const bool resc = __any(mx[0] > m_run[0] + kRescale || mx[1] > m_run[1] + kRescale);
+      const bool resc = i == 0 || __any(mx[0] > kRescale || mx[1] > kRescale);
       if (resc) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const float m_new = fmaxf(m_run[qb], mx[qb]);
-          const float al = fast_exp2(m_run[qb] - m_new);   // m_run = -inf -> 0
+          const float m_new = set_m(qb, m_run[qb] + (i == 0 ? mx[qb] : fmaxf(mx[qb], 0.0f)));
+          const float shift = m_new - m_run[qb];
+          const float al = i == 0 ? 0.0f : fast_exp2(-shift);
           m_run[qb] = m_new;
           if (hi == 0) alpha_s[bi * 64 + qb * 32 + l32] = al;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) s[kb2][qb][k] -= shift;
         }
       }
       if (lane == 0) flag_s[bi] = resc ? 1 : 0;
@@ -612,7 +642,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
           for (int half = 0; half < 2; ++half) {
             float e[8];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) e[x] = fast_exp2(fmaf(s[kb2][qb][half * 8 + x], c, -m_run[qb]));
+            for (int x = 0; x < 8; ++x) e[x] = fast_exp2(s[kb2][qb][half * 8 + x]);
             const int ks = kb2 * 2 + half;
             *(bf16x8*)(pw + ((qb * 4 + ks) * 64 + lane) * 16) = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
           }
