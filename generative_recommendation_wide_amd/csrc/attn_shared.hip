@@ -566,10 +566,21 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
     for (int i = 0; i <= ntiles; ++i) {
       lds::wait_all_vm();
       __syncthreads();
+      const uint8_t* st = smem + KRING + (i & 1) * TILE_BYTES;
+      bf16x8 kf[2][2][4];   // [half of D][key block][k-step of the half]
+      auto read_kf = [&](int h2) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int lc = 2 * (h2 * 4 + k4) + hi;
+          kf[h2][0][k4] = *(const bf16x8*)(st + l32 * 256 + ((lc ^ (l32 & 15)) << 4));
+          kf[h2][1][k4] = *(const bf16x8*)(st + (32 + l32) * 256 + ((lc ^ (l32 & 15)) << 4));
+        }
+      };
+      // the first fragments' LDS latency passes while the tile loads are issued
+      if (i < ntiles) read_kf(0);
       if (i + 1 < ntiles) issue_k(smem + KRING + ((i + 1) & 1) * TILE_BYTES, kb, p0 + (i + 1) * NT, wave, toff);
       if (i < ntiles) issue_v(smem + VRING + (i & 1) * TILE_BYTES, vb, p0 + i * NT, wave, toff);
       if (i == ntiles) break;
-      const uint8_t* st = smem + KRING + (i & 1) * TILE_BYTES;
       const int p = p0 + i * NT;
       floatx16 s[2][2];   // [key block][row block]
       __builtin_amdgcn_s_setprio(2);
@@ -579,20 +590,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
         for (int qb = 0; qb < 2; ++qb) s[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, qm[qb], floatx16{}, 0, 0, 0);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 kf[2][4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const int lc = 2 * (h2 * 4 + k4) + hi;
-          kf[0][k4] = *(const bf16x8*)(st + l32 * 256 + ((lc ^ (l32 & 15)) << 4));
-          kf[1][k4] = *(const bf16x8*)(st + (32 + l32) * 256 + ((lc ^ (l32 & 15)) << 4));
-        }
+        if (h2 == 1) read_kf(1);
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
           for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
-              s[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb2][k4], qf[qb][h2 * 4 + k4], s[kb2][qb], 0, 0, 0);
+              s[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[h2][kb2][k4], qf[qb][h2 * 4 + k4], s[kb2][qb], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
       // value k of key block kb2 is key p + kb2*32 + (k/8)*16 + hi*8 + ((k/4)%2)*4 + k%4
