@@ -647,7 +647,7 @@ def mfma_ceiling(dev, launches=8, iters=20000):
     lib.grw_ceiling_mfma_per_round.restype = ctypes.c_int
     blocks = torch.cuda.get_device_properties(dev).multi_processor_count
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    ts = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
+    ts = torch.zeros(blocks * 4, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     if lib.grw_ceiling_mfma(blocks, iters, out.data_ptr(), ts.data_ptr(), sp) != 0:
@@ -663,18 +663,28 @@ def mfma_ceiling(dev, launches=8, iters=20000):
     per_round = lib.grw_ceiling_mfma_per_round()
     mfmas_per_wave = per_round * iters
     flops = 32768.0 * mfmas_per_wave * 4 * blocks
-    # the clock ramps up under sustained load: the rate and the clock are those of the last launch
-    tf = flops / (ev[launches - 1].elapsed_time(ev[launches]) / 1e3) / 1e12
-    t = ts.cpu().numpy().reshape(blocks, 2).astype(np.float64)
+    # the clock ramps up under sustained load: everything is taken from the last launch.  The
+    # rate is over the workgroups' own span (first loop start to last loop end, 100 MHz
+    # s_memrealtime): the launch as HIP events see it is about 1 ms longer whatever its length
+    # (a fixed per-launch cost outside the loops), which is no property of the MFMA pipes.
+    t = ts.cpu().numpy().reshape(blocks, 4).astype(np.float64)
+    span_us = float(t[:, 3].max() - t[:, 2].min()) / 100.0
+    tf = flops / (span_us / 1e6) / 1e12
     ghz = float(np.median(t[:, 0] / (t[:, 1] * 10.0)))
     cyc = float(np.median(t[:, 0] / mfmas_per_wave))
+    dur_us = t[:, 1] / 100.0
     peak_at_clock = 1024.0 * 1024 * ghz * 1e9 / 1e12
     return {"mfma_bf16_TFLOPs": round(tf, 1), "mfma_bf16_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "mfma_cycles_per_32x32x16": round(cyc, 2), "shader_clock_GHz_under_mfma_load": round(ghz, 3),
+            "workgroup_loop_us_min_median_max": [round(float(dur_us.min()), 1), round(float(np.median(dur_us)), 1),
+                                                 round(float(dur_us.max()), 1)],
+            "first_start_to_last_end_us": round(span_us, 1),
+            "launch_us_hip_events": round(ev[launches - 1].elapsed_time(ev[launches]) * 1e3, 1),
             "dense_bf16_peak_at_that_clock_TFLOPs": round(peak_at_clock, 1),
             "mfma_how": (f"libgrw_ceiling.so probe: {blocks} workgroups x 4 waves, {per_round} independent "
                          f"32x32x16 bf16 accumulations per wave, {iters} rounds, {launches} launches back to back; "
-                         "rate and clock (s_memtime cycles / s_memrealtime 100 MHz ticks) of the last launch")}
+                         "rate over the last launch's workgroup span (s_memrealtime, 100 MHz), clock = s_memtime "
+                         "cycles / s_memrealtime ticks of its loops")}
 
 
 def unshared_roofline(wl, st, t_ms):
