@@ -203,7 +203,7 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, const ShWork& w
         const int bb = mr / g;
         const int qq = h * g + (mr - bb * g);
         float* dst = a.opart + (((size_t)wk.split * a.sumW + rd.boff + bb) * Hq + qq) * DH;
-        *(floatx4*)(dst + half * 64 + rch * 4) = v;
+        __builtin_nontemporal_store(v, (floatx4*)(dst + half * 64 + rch * 4));   // read back by the next launch only
       }
     }
     __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);   // reads done before the next half overwrites
@@ -488,7 +488,7 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, const ShWork& wk, 
         const int bb = mr / g;
         const int qq = h * g + (mr - bb * g);
         float* dst = a.opart + (((size_t)wk.split * a.sumW + rd.boff + bb) * Hq + qq) * DH;
-        *(floatx4*)(dst + half * 64 + rch * 4) = v;
+        __builtin_nontemporal_store(v, (floatx4*)(dst + half * 64 + rch * 4));   // read back by the next launch only
       }
     }
     __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15);
