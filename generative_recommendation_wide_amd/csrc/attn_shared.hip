@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_shared_mfma_kernel(AttnArgs a, co
       }
     }
     float mx = max32(s0, s1);
-    mx = vmax(mx, __shfl_xor(mx, 32, 64)) * c;
+    mx = half_swap_max(mx) * c;
     // Lazy rescale: the running max m_run only moves when some row's tile max exceeds it
     // by more than kRescale (log2 units), so p = 2^(s*c - m_run) <= 2^kRescale and the
     // O / l rescale runs on a few tiles only (wave-uniform branch).
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const float m = max32(s[0][qb], s[1][qb]);
-        mx[qb] = vmax(m, __shfl_xor(m, 32, 64));
+        mx[qb] = half_swap_max(m);
       }
       // Lazy rescale as in the kernels above: m moves when some row's x exceeds kRescale (on
       // the first tile, to the tile max); then x drops by the shift and the product wave

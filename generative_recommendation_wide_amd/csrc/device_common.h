@@ -89,6 +89,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Maximum that propagates NaN (IEEE 754-2019 maximum).  Chains of it lower to
 // v_maximum3_f32; fmaxf on MFMA results costs an extra canonicalising v_max per operand.
+// max(x[l], x[l ^ 32]) in every lane l: the two 32-lane halves exchanged in registers
+// (v_permlane32_swap of x with itself leaves x[l] and x[l ^ 32] in the pair), with no LDS
+// round trip as a cross-half shuffle takes.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
