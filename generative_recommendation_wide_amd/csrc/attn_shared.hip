@@ -174,7 +174,7 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, const ShWork& w
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = a.g, Hq = a.Hq, h = wk.h;
   const int nrows = rd.W * g;
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float l = l_run + lane_xor<32>(l_run);
   const float inv = row_ok ? out_scale / l : 0.0f;
   if (row_ok && hi == 0) a.lpart[((size_t)wk.split * a.sumW + slot) * Hq + qh] = (m_run + fast_log2(l)) * kLn2;
   uint8_t* tb = smem + wave * 8192;
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_shared_split_kernel(AttnA
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float m = alpha_s[sw * 64 + qb * 32 + l32];
-      const float l = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+      const float l = l_run[qb] + lane_xor<32>(l_run[qb]);
       store_rows(a, wk, rd, smem + KRING + sw * TILE_BYTES, o[qb], m, l, wk.m0 + sw * 64 + qb * 32);
     }
   }

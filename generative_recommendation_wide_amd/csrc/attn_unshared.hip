@@ -141,7 +141,13 @@ __global__ __launch_bounds__(256) void attn_unshared_kernel(AttnArgs a) {
       float s = 0.0f;
 #pragma unroll
       for (int i = 0; i < E; ++i) s = fmaf(q[jj][i], kx[i], s);
-      for (int w = 1; w < LPH; w <<= 1) s += __shfl_xor(s, w, 64);
+      // sum over the head's LPH lanes (xor distances 1, 2, ... below LPH; LPH is wave-uniform)
+      if (LPH > 1) s += lane_xor<1>(s);
+      if (LPH > 2) s += lane_xor<2>(s);
+      if (LPH > 4) s += lane_xor<4>(s);
+      if (LPH > 8) s += lane_xor<8>(s);
+      if (LPH > 16) s += lane_xor<16>(s);
+      if (LPH > 32) s += lane_xor<32>(s);
       s *= c;
       const float mn = fmaxf(m[jj], s);
       const float alpha = fast_exp2(m[jj] - mn);

@@ -44,10 +44,21 @@ namespace grw {
 
 namespace {
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
+// hist[d] += 1 for every active lane with `on` set.  The lanes whose digit equals that of
+// the wave's first such lane are counted with one atomic, the others one by one.  Used for
+// a radix select's first digit, which clusters (for float keys it is mostly the exponent):
+// same-address LDS atomics of one instruction serialise.  Later digits are spread, and
+// there the extra ballots cost more than they save.  Divergence-safe (the lane masks cover
+// the active lanes only).
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool on) {
+  const uint64_t act = __ballot(on);
+  if (act == 0) return;
+  const int first = __builtin_ctzll(act);
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);
+  const bool same = on && d == d0;
+  const uint64_t m = __ballot(same);
+  if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(m));
+  else if (on && !same) atomicAdd(&hist[d], 1u);
 }
 
 // Pick, from a 256-bucket histogram, the digit whose bucket holds the `need`-th largest
@@ -86,7 +97,9 @@ __device__ __forceinline__ uint64_t block_select_threshold(Get get, int n, int N
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint64_t v = get(i);
-      if (v != 0 && (v & mask) == prefix) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
+      const bool on = v != 0 && (v & mask) == prefix;
+      if (mask == 0) hist_add(hist, (uint32_t)(v >> shift) & 255u, on);
+      else if (on) atomicAdd(&hist[(uint32_t)(v >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) pick_digit(hist, need, scr);
@@ -105,11 +118,8 @@ __device__ __forceinline__ uint64_t block_select_threshold(Get get, int n, int N
 template <int NT>
 __device__ __forceinline__ void block_or_and(uint64_t& o, uint64_t& an, uint64_t* red) {
   constexpr int NW = NT / 64;
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) {
-    o |= shfl_xor_u64(o, s);
-    an &= shfl_xor_u64(an, s);
-  }
+  o = wave_butterfly(o, [](uint64_t x, uint64_t y) { return x | y; });
+  an = wave_butterfly(an, [](uint64_t x, uint64_t y) { return x & y; });
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { red[wave] = o; red[NW + wave] = an; }
@@ -183,13 +193,15 @@ __device__ __forceinline__ uint64_t regs_select_threshold(Get get, int N, uint32
   uint64_t prefix = o & known;
   uint32_t need = (uint32_t)N;
   int shift = hb >= 7 ? hb - 7 : 0;
-  while (true) {
+  for (bool first = true;; first = false) {
     for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const uint64_t x = get(k);
-      if (x != 0 && (x & known) == prefix) atomicAdd(&hist[(uint32_t)(x >> shift) & 255u], 1u);
+      const bool on = x != 0 && (x & known) == prefix;
+      if (first) hist_add(hist, (uint32_t)(x >> shift) & 255u, on);
+      else if (on) atomicAdd(&hist[(uint32_t)(x >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) pick_digit(hist, need, scr);
@@ -221,11 +233,8 @@ __device__ __forceinline__ Sel32 regs_select32(Get get, uint32_t N, uint32_t n, 
     const uint32_t x = get(k);
     if (x) { o |= x; an &= x; }
   }
-#pragma unroll
-  for (int sh = 32; sh > 0; sh >>= 1) {
-    o |= __shfl_xor(o, sh, 64);
-    an &= __shfl_xor(an, sh, 64);
-  }
+  o = wave_butterfly(o, [](uint32_t x, uint32_t y) { return x | y; });
+  an = wave_butterfly(an, [](uint32_t x, uint32_t y) { return x & y; });
   __syncthreads();
   if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = o; red[NW + (threadIdx.x >> 6)] = an; }
   __syncthreads();
@@ -241,13 +250,15 @@ __device__ __forceinline__ Sel32 regs_select32(Get get, uint32_t N, uint32_t n, 
   uint32_t prefix = o & known;
   uint32_t need = N;
   int shift = hb >= 7 ? hb - 7 : 0;
-  while (true) {
+  for (bool first = true;; first = false) {
     for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const uint32_t x = get(k);
-      if (x != 0 && (x & known) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+      const bool on = x != 0 && (x & known) == prefix;
+      if (first) hist_add(hist, (x >> shift) & 255u, on);
+      else if (on) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (threadIdx.x < 64) pick_digit(hist, need, scr);
@@ -281,10 +292,10 @@ template <int NE>
 __device__ __forceinline__ void block_append(uint64_t* dst, int* counter, const uint64_t (&e)[NE], int ne) {
   const int lane = threadIdx.x & 63;
   const int incl = wave_inclusive_scan(ne);
-  const int total = __shfl(incl, 63, 64);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
   int base = 0;
   if (lane == 63 && total > 0) base = atomicAdd(counter, total);
-  base = __shfl(base, 63, 64);
+  base = __builtin_amdgcn_readlane(base, 63);
   const int pos = base + incl - ne;
 #pragma unroll
   for (int k = 0; k < NE; ++k)
@@ -729,7 +740,12 @@ __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S)
   }
   // one contribution per group of gsz threads (at most top_k per beam)
   const int gl = gsz < 64 ? gsz : 64;
-  for (int o = 1; o < gl; o <<= 1) best = max(best, shfl_xor_u64(best, o));
+  if (gl > 1) best = max(best, lane_xor<1>(best));
+  if (gl > 2) best = max(best, lane_xor<2>(best));
+  if (gl > 4) best = max(best, lane_xor<4>(best));
+  if (gl > 8) best = max(best, lane_xor<8>(best));
+  if (gl > 16) best = max(best, lane_xor<16>(best));
+  if (gl > 32) best = max(best, lane_xor<32>(best));
   if (gsz > 64) {
     if ((tid & 63) == 0) red64[tid >> 6] = best;
     __syncthreads();
@@ -1007,8 +1023,7 @@ __global__ __launch_bounds__(256) void select_topk_kernel(SelArgs a) {
     }
   }
   if (tid == 0) a.surv_count[slot] = n_out;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  fl = wave_butterfly(fl, [](int x, int y) { return x | y; });
   if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
 }
 
@@ -1108,8 +1123,27 @@ struct FinalLds {
 // every winner its output position.  When a bin holds more than BINCAP entries, a radix
 // select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
 // device-coherent loads (they may come from other workgroups of the same kernel).
+// Survivor counts of request r's beams tid * BPT + k (device-coherent loads: the per-beam
+// stage and the overflow rows write them) and the thread's best live beam score as an
+// ordered key (0 if none).
+template <int NT, int MAXW>
+__device__ __forceinline__ uint32_t final_counts(const SelArgs& a, const ReqDesc& rd, int32_t (&cnt)[MAXW / NT]) {
+  uint32_t smax = 0;
+#pragma unroll
+  for (int k = 0; k < MAXW / NT; ++k) {
+    const int b = (int)threadIdx.x * (MAXW / NT) + k;
+    cnt[k] = b < rd.W ? ld_dev(&a.surv_count[rd.boff + b]) : 0;
+    if (b < rd.W) {
+      const float sc = a.scores[rd.boff + b];
+      if (sc != -INFINITY && !__builtin_isnan(sc)) smax = max(smax, ordered_key(sc));
+    }
+  }
+  return smax;
+}
+
 template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP, bool G = false, bool X = false>
-__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L) {
+__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L,
+                                             const int32_t (&cnt)[MAXW / NT], uint32_t smax) {
   constexpr bool EDGES = EDGECAP == WINCAP;   // entries carry their CSR edge (trie rows)
   constexpr int BPT = MAXW / NT;     // beams per thread
   constexpr int HPT = NB / NT;       // bins per thread
@@ -1118,19 +1152,15 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
   const ReqDesc rd = a.req[r];
   const int W = rd.W, K = keep_k(a, rd);
   const uint64_t* pool = a.pool + rd.pool_off;
+  const uint32_t bound = ld_dev(&a.bound[r]);
 
   // beam prefix of the survivor counts, best live score
   uint32_t cb[BPT];
-  uint32_t csum = 0, smax = 0;
+  uint32_t csum = 0;
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    const int b = tid * BPT + k;
-    cb[k] = b < W ? min((uint32_t)ld_dev(&a.surv_count[rd.boff + b]), (uint32_t)K) : 0u;
+    cb[k] = min((uint32_t)cnt[k], (uint32_t)K);
     csum += cb[k];
-    if (b < W) {
-      const float sc = a.scores[rd.boff + b];
-      if (sc != -INFINITY && !__builtin_isnan(sc)) smax = max(smax, ordered_key(sc));
-    }
   }
   {
     const uint32_t incl = (uint32_t)wave_inclusive_scan((int)csum);
@@ -1213,7 +1243,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
 
   // histogram origin and scale: bins reach from the best live score (the best entry with
   // noise) down to the bound
-  uint32_t lo = ld_dev(&a.bound[r]);
+  uint32_t lo = bound;
   if (lo == 0 && smax != 0) {
     const uint32_t u = (smax & 0x80000000u) ? (smax & 0x7fffffffu) : ~smax;   // inverse ordered key
     lo = ordered_key(__uint_as_float(u) - 64.0f);
@@ -1225,49 +1255,41 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
   for_each_entry([&](uint64_t v, int) { atomicAdd(&L.hcnt[hist_bin<NB>(v, org, scale)], 1u); });
   __syncthreads();
 
-  // bin starts: exclusive scan of the histogram; the bin of the nsel-th entry
-  uint32_t c[HPT];
+  // bin starts: exclusive scan of the histogram; the bin tb of the nsel-th entry and, from a
+  // prefix maximum taken in the same pass, the largest count among bins <= tb
   {
-    uint32_t tsum = 0;
+    uint32_t c[HPT];
+    uint32_t tsum = 0, tmax = 0;
 #pragma unroll
-    for (int k = 0; k < HPT; ++k) { c[k] = L.hcnt[tid * HPT + k]; tsum += c[k]; }
+    for (int k = 0; k < HPT; ++k) { c[k] = L.hcnt[tid * HPT + k]; tsum += c[k]; tmax = max(tmax, c[k]); }
     const uint32_t incl = (uint32_t)wave_inclusive_scan((int)tsum);
+    const uint32_t imax = wave_inclusive_max_scan(tmax);
     __syncthreads();
-    if (lane == 63) L.wsum[wave] = incl;
+    if (lane == 63) { L.wsum[wave] = incl; L.wmax[wave] = imax; }
     __syncthreads();
     uint32_t run = incl - tsum;
-    for (int w = 0; w < wave; ++w) run += L.wsum[w];
+    uint32_t pmax = lane_before(imax);   // maximum over the earlier lanes' bins
+    for (int w = 0; w < wave; ++w) { run += L.wsum[w]; pmax = max(pmax, L.wmax[w]); }
 #pragma unroll
     for (int k = 0; k < HPT; ++k) {
+      pmax = max(pmax, c[k]);
       L.start[tid * HPT + k] = run;
-      if (nsel > 0 && run < (uint32_t)nsel && (uint32_t)nsel <= run + c[k]) L.tb = tid * HPT + k;
+      if (nsel > 0 && run < (uint32_t)nsel && (uint32_t)nsel <= run + c[k]) { L.tb = tid * HPT + k; L.maxc = pmax; }
       run += c[k];
     }
     if (tid == NT - 1) L.start[NB] = run;
   }
   __syncthreads();
   const uint32_t tb = L.tb;
-  {
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < HPT; ++k)
-      if ((uint32_t)(tid * HPT + k) <= tb) m = max(m, c[k]);
-    m = wave_max(m);
-    if (lane == 0 && m) atomicMax(&L.maxc, m);
-  }
-  __syncthreads();
   const bool fast = nsel > 0 && tb < (uint32_t)NB && L.maxc <= (uint32_t)BINCAP && L.start[tb + 1] <= (uint32_t)WINCAP;
 
   if (fast) {
-    // place every entry of bins <= tb in its bin's segment, then rank it inside the bin
-    uint32_t* cursor = L.hcnt;
-#pragma unroll
-    for (int k = 0; k < HPT; ++k) cursor[tid * HPT + k] = 0u;
-    __syncthreads();
+    // place every entry of bins <= tb in its bin's segment (counting the bin's count down),
+    // then rank it inside the bin
     auto place = [&](uint64_t v, int e) {
       const int b = hist_bin<NB>(v, org, scale);
       if ((uint32_t)b <= tb) {
-        const uint32_t p = L.start[b] + atomicAdd(&cursor[b], 1u);
+        const uint32_t p = L.start[b] + atomicSub(&L.hcnt[b], 1u) - 1u;
         if (p < L.start[b + 1]) {
           L.win[p] = v;
           if constexpr (EDGES) L.wedge[p] = e;
@@ -1341,7 +1363,9 @@ template <bool G, bool X>
 __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GlobLds& L = *(GlobLds*)smem;
-  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G, X>(a, blockIdx.x, L);
+  int32_t cnt[kMaxW / kGlobThreads];
+  const uint32_t smax = final_counts<kGlobThreads, kMaxW>(a, a.req[blockIdx.x], cnt);
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G, X>(a, blockIdx.x, L, cnt, smax);
   if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
 }
 
@@ -1634,8 +1658,7 @@ __global__ __launch_bounds__(256) void select_pilot_beam_kernel(SelArgs a) {
     if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, true, S.redf, S.redd, fl);
   const int n_out = keep_beam<L, G>(a, b, rr, fl, S.red, S.hist, S.scr, S.red32, mwords, mprefix);
   if (tid == 0) a.surv_count[slot] = n_out;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  fl = wave_butterfly(fl, [](int x, int y) { return x | y; });
   if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
 }
 
@@ -1653,21 +1676,29 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   __shared__ int n_over;
   const int r = blockIdx.x;
   const ReqDesc rd = a.req[r];
-  // beams whose rows overflowed top_k: their survivors first (listed in L.pre meanwhile)
+  constexpr int BPT = kFusedMaxW / kFinThreads;
+  int32_t cnt[BPT];
+  uint32_t smax = final_counts<kFinThreads, kFusedMaxW>(a, rd, cnt);
+  // beams whose rows overflowed top_k (negative counts): their survivors first (listed in
+  // L.pre meanwhile); the counts are read again after them
   if (threadIdx.x == 0) n_over = 0;
   __syncthreads();
-  for (int jj = threadIdx.x; jj < rd.W; jj += kFinThreads)
-    if (a.surv_count[rd.boff + jj] < 0) L.pre[atomicAdd(&n_over, 1)] = (uint32_t)(rd.boff + jj);
+#pragma unroll
+  for (int k = 0; k < BPT; ++k)
+    if (cnt[k] < 0) L.pre[atomicAdd(&n_over, 1)] = (uint32_t)(rd.boff + (int)threadIdx.x * BPT + k);
   __syncthreads();
   const int no = n_over;
-  for (int i = 0; i < no; ++i) {
-    const int slot = (int)L.pre[i];
+  if (no > 0) {
+    for (int i = 0; i < no; ++i) {
+      const int slot = (int)L.pre[i];
+      __syncthreads();
+      overflow_row<kFinThreads, kOnePass / kFinThreads, G, X>(a, rd, r, slot, L.hist, L.scr, red32, red);
+    }
+    wait_stores();
     __syncthreads();
-    overflow_row<kFinThreads, kOnePass / kFinThreads, G, X>(a, rd, r, slot, L.hist, L.scr, red32, red);
+    smax = final_counts<kFinThreads, kFusedMaxW>(a, rd, cnt);
   }
-  wait_stores();
-  __syncthreads();
-  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, L);
+  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, L, cnt, smax);
   __syncthreads();
   if (threadIdx.x == 0) a.bound[r] = 0u;
   if (threadIdx.x < kSyncCopies) a.sync[((size_t)r * kSyncCopies + threadIdx.x) * kSyncStride] = 0ull;
@@ -1701,8 +1732,7 @@ __global__ __launch_bounds__(256) void select_lse_kernel(SelArgs a) {
   if (lane == 0) redd[wave] = sum;
   __syncthreads();
   if (threadIdx.x == 0) a.row_lse[slot] = (float)(md + log(((redd[0] + redd[1]) + redd[2]) + redd[3]));
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) fl |= __shfl_xor(fl, o, 64);
+  fl = wave_butterfly(fl, [](int x, int y) { return x | y; });
   if (lane == 0 && fl) atomicOr(a.flags, fl);
 }
 
