@@ -559,13 +559,29 @@ __device__ __forceinline__ uint64_t loaded_row_best(RowRegs<L, G>& rr, const Sel
                                                     int cnt, float s, uint32_t flat_base, int& fl, float* redf,
                                                     double* redd) {
   if constexpr (X) to_logprobs<L, G>(rr, a, slot, lprow, a.lse_ready == 0, redf, redd, fl);
-  uint64_t best = 0;
+  if constexpr (L == kTrie) {
+    uint64_t best = 0;
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k) {
-    const uint32_t o = row_key<L>(rr, k, cnt, s, 0u, fl);
-    if (o) best = max(best, composite_key(o, flat_base + (uint32_t)rr.code_of(k)));
+    for (int k = 0; k < kRegC; ++k) {
+      const uint32_t o = row_key<L>(rr, k, cnt, s, 0u, fl);
+      if (o) best = max(best, composite_key(o, flat_base + (uint32_t)rr.code_of(k)));
+    }
+    return best;
+  } else {
+    // full rows: a thread's codes rise with k, so the largest composite is the largest
+    // ordered key at the smallest k that holds it
+    uint32_t ok[kRegC];
+    uint32_t om = 0u;
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      ok[k] = row_key<L>(rr, k, cnt, s, 0u, fl);
+      om = max(om, ok[k]);
+    }
+    int kb = 0;
+#pragma unroll
+    for (int k = kRegC - 1; k >= 0; --k) kb = ok[k] == om ? k : kb;
+    return om ? composite_key(om, flat_base + (uint32_t)rr.code_of(kb)) : 0ull;
   }
-  return best;
 }
 
 // The best candidate of a row of up to kOnePass candidates (0 when none).
@@ -1426,10 +1442,39 @@ __device__ __forceinline__ BeamRow beam_setup(const SelArgs& a, int slot, int& f
 // request's W-of-pool workgroup selects that row's top_k; with noise (G), where it happens
 // to several beams per step, a radix select over the registers keeps the top_k here.
 // Reached by every thread of the workgroup.
+// What a thread of a beam workgroup can learn from its loaded row before the bound is
+// known: its largest ordering key (NaN keys ignored; -inf when it holds none) and whether
+// any of its positions holds a NaN or positive log-probability.
+struct RowPre {
+  float best;
+  bool suspect;
+};
 template <int L, bool G>
-__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L, G>& rr, int& fl, int* red,
-                                         uint32_t* hist, uint32_t* scr, uint32_t* red32, uint32_t* mwords,
-                                         uint32_t* mprefix) {
+__device__ __forceinline__ RowPre row_pre(const BeamRow& b, const RowRegs<L, G>& rr) {
+  RowPre p{-INFINITY, false};
+  if constexpr (G) {
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      p.suspect |= !(rr.lp[k] <= 0.0f);
+      p.best = fmaxf(p.best, order_key<G>(b.s + rr.lp[k], rr.tg[k]));
+    }
+  } else {
+    // rounded addition is monotonic: the largest s + lp is s + the largest lp
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kRegC; ++k) {
+      p.suspect |= !(rr.lp[k] <= 0.0f);
+      m = fmaxf(m, rr.lp[k]);
+    }
+    p.best = b.s + m;
+  }
+  return p;
+}
+
+template <int L, bool G>
+__device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, const RowRegs<L, G>& rr, const RowPre& pre,
+                                         int& fl, int* red, uint32_t* hist, uint32_t* scr, uint32_t* red32,
+                                         uint32_t* mwords, uint32_t* mprefix) {
   const ReqDesc& rd = b.rd;
   const uint32_t tau = b.tau;
   // a beam below the bound keeps nothing: no key exceeds its beam's score (with noise an
@@ -1442,15 +1487,13 @@ __device__ __forceinline__ int keep_beam(const SelArgs& a, const BeamRow& b, con
   // of positions without a candidate never pass.  Most rows admit a handful of candidates,
   // so ordered keys are formed only for those.
   const float tau_f = tau < 0x00800000u ? -3.402823466e+38f : float_of_ordered(tau);   // -FLT_MAX: every finite key
+  // only a thread whose best key reaches the bound looks at its positions
   int na = 0;
-  bool suspect = false;
+  if (pre.best >= tau_f) {
 #pragma unroll
-  for (int k = 0; k < kRegC; ++k) {
-    const float lp = rr.lp[k];
-    suspect |= !(lp <= 0.0f);                    // NaN or positive: a precondition flag
-    na += order_key<G>(b.s + lp, G ? rr.tg[k] : 0.0f) >= tau_f;
+    for (int k = 0; k < kRegC; ++k) na += order_key<G>(b.s + rr.lp[k], G ? rr.tg[k] : 0.0f) >= tau_f;
   }
-  if (suspect) {
+  if (pre.suspect) {                             // NaN or positive: a precondition flag
 #pragma unroll
     for (int k = 0; k < kRegC; ++k) {
       if (__builtin_isnan(rr.lp[k])) fl |= GRW_FLAG_NAN_LOGPROB;
@@ -1626,8 +1669,13 @@ __device__ __forceinline__ uint64_t wait_sync(const SelArgs& a, int r, uint64_t 
   return v;
 }
 
+// Waves per SIMD the pilot + per-beam kernel is built for: with plain full rows every beam
+// workgroup's row fits in 64 registers per lane, so 8 workgroups per CU are resident.
 template <int L, bool G, bool X>
-__global__ __launch_bounds__(256) void select_pilot_beam_kernel(SelArgs a) {
+constexpr int pilot_beam_waves() { return (L == kFull && !G && !X) ? 8 : 1; }
+
+template <int L, bool G, bool X>
+__global__ __launch_bounds__(256, (pilot_beam_waves<L, G, X>())) void select_pilot_beam_kernel(SelArgs a) {
   __shared__ PilotLds S;
   __shared__ uint32_t mwords[L == kTrie ? 256 : 1];
   __shared__ uint32_t mprefix[L == kTrie ? 256 : 1];
@@ -1649,14 +1697,16 @@ __global__ __launch_bounds__(256) void select_pilot_beam_kernel(SelArgs a) {
   } else if (b.live) {
     fl |= lfl;
   }
-  // a dead or non-expanding slot keeps nothing and needs no bound (b.live is uniform)
-  const uint64_t w = b.live ? wait_sync(a, b.r, kSyncBound, &word_s) : 0ull;
-  b.tau = (w & kSyncBound) ? (uint32_t)w : 0u;
   // every slot computes its own row lse (a pilot slot's equals its pilot's: same layout, same
   // reduction order)
   if constexpr (X)
     if (b.live) to_logprobs<L, G>(rr, a, slot, b.lprow, true, S.redf, S.redd, fl);
-  const int n_out = keep_beam<L, G>(a, b, rr, fl, S.red, S.hist, S.scr, S.red32, mwords, mprefix);
+  // the work that does not need the bound is done while the pilots finish
+  const RowPre pre = b.live ? row_pre<L, G>(b, rr) : RowPre{-INFINITY, false};
+  // a dead or non-expanding slot keeps nothing and needs no bound (b.live is uniform)
+  const uint64_t w = b.live ? wait_sync(a, b.r, kSyncBound, &word_s) : 0ull;
+  b.tau = (w & kSyncBound) ? (uint32_t)w : 0u;
+  const int n_out = keep_beam<L, G>(a, b, rr, pre, fl, S.red, S.hist, S.scr, S.red32, mwords, mprefix);
   if (tid == 0) a.surv_count[slot] = n_out;
   fl = wave_butterfly(fl, [](int x, int y) { return x | y; });
   if ((tid & 63) == 0 && fl) atomicOr(a.flags, fl);
