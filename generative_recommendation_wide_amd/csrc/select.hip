@@ -46,9 +46,11 @@ namespace {
 
 // hist[d] += 1 for every active lane with `on` set.  The lanes whose digit equals that of
 // the wave's first such lane are counted with one atomic, the others one by one.  Used for
-// a radix select's first digit, which clusters (for float keys it is mostly the exponent):
-// same-address LDS atomics of one instruction serialise.  Later digits are spread, and
-// there the extra ballots cost more than they save.  Divergence-safe (the lane masks cover
+// a radix select's first digit when that digit lies in the sign and exponent bits of an
+// ordered float key: such digits cluster in one or two values (three quarters of a
+// log-probability row's 8192 keys share one), and same-address LDS atomics of one
+// instruction serialise.  Mantissa digits are spread, and there the extra ballots and the
+// second atomic cost several times what they save.  Divergence-safe (the lane masks cover
 // the active lanes only).
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool on) {
   const uint64_t act = __ballot(on);
@@ -200,7 +202,7 @@ __device__ __forceinline__ uint64_t regs_select_threshold(Get get, int N, uint32
     for (int k = 0; k < NR; ++k) {
       const uint64_t x = get(k);
       const bool on = x != 0 && (x & known) == prefix;
-      if (first) hist_add(hist, (uint32_t)(x >> shift) & 255u, on);
+      if (first && shift >= 55) hist_add(hist, (uint32_t)(x >> shift) & 255u, on);
       else if (on) atomicAdd(&hist[(uint32_t)(x >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -257,7 +259,7 @@ __device__ __forceinline__ Sel32 regs_select32(Get get, uint32_t N, uint32_t n, 
     for (int k = 0; k < NR; ++k) {
       const uint32_t x = get(k);
       const bool on = x != 0 && (x & known) == prefix;
-      if (first) hist_add(hist, (x >> shift) & 255u, on);
+      if (first && shift >= 23) hist_add(hist, (x >> shift) & 255u, on);
       else if (on) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
