@@ -1142,10 +1142,15 @@ struct FinalLds {
 // select and a bitonic sort in LDS do the same job.  Pool entries and counts are read with
 // device-coherent loads (they may come from other workgroups of the same kernel).
 // Survivor counts of request r's beams tid * BPT + k (device-coherent loads: the per-beam
-// stage and the overflow rows write them) and the thread's best live beam score as an
-// ordered key (0 if none).
+// stage and the overflow rows write them), the thread's best live beam score as an ordered
+// key (0 if none) and the request's bound, all in one round of loads.
+struct FinalIn {
+  uint32_t smax, bound;
+};
+
 template <int NT, int MAXW>
-__device__ __forceinline__ uint32_t final_counts(const SelArgs& a, const ReqDesc& rd, int32_t (&cnt)[MAXW / NT]) {
+__device__ __forceinline__ FinalIn final_counts(const SelArgs& a, int r, const ReqDesc& rd, int32_t (&cnt)[MAXW / NT]) {
+  const uint32_t bound = ld_dev(&a.bound[r]);
   uint32_t smax = 0;
 #pragma unroll
   for (int k = 0; k < MAXW / NT; ++k) {
@@ -1156,21 +1161,21 @@ __device__ __forceinline__ uint32_t final_counts(const SelArgs& a, const ReqDesc
       if (sc != -INFINITY && !__builtin_isnan(sc)) smax = max(smax, ordered_key(sc));
     }
   }
-  return smax;
+  return FinalIn{smax, bound};
 }
 
 template <int NT, int NB, int MAXW, int WINCAP, int BINCAP, int EDGECAP, bool G = false, bool X = false>
-__device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L,
-                                             const int32_t (&cnt)[MAXW / NT], uint32_t smax) {
+__device__ __forceinline__ void final_select(const SelArgs& a, int r, const ReqDesc& rd,
+                                             FinalLds<NT, NB, MAXW, WINCAP, EDGECAP>& L, const int32_t (&cnt)[MAXW / NT],
+                                             const FinalIn in) {
   constexpr bool EDGES = EDGECAP == WINCAP;   // entries carry their CSR edge (trie rows)
   constexpr int BPT = MAXW / NT;     // beams per thread
   constexpr int HPT = NB / NT;       // bins per thread
   constexpr int NRG = 8;             // pool entries cached per thread (and per batch beyond)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const ReqDesc rd = a.req[r];
   const int W = rd.W, K = keep_k(a, rd);
   const uint64_t* pool = a.pool + rd.pool_off;
-  const uint32_t bound = ld_dev(&a.bound[r]);
+  uint32_t smax = in.smax;
 
   // beam prefix of the survivor counts, best live score
   uint32_t cb[BPT];
@@ -1261,7 +1266,7 @@ __device__ __forceinline__ void final_select(const SelArgs& a, int r, FinalLds<N
 
   // histogram origin and scale: bins reach from the best live score (the best entry with
   // noise) down to the bound
-  uint32_t lo = bound;
+  uint32_t lo = in.bound;
   if (lo == 0 && smax != 0) {
     const uint32_t u = (smax & 0x80000000u) ? (smax & 0x7fffffffu) : ~smax;   // inverse ordered key
     lo = ordered_key(__uint_as_float(u) - 64.0f);
@@ -1382,8 +1387,9 @@ __global__ __launch_bounds__(kGlobThreads) void select_global_kernel(SelArgs a) 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GlobLds& L = *(GlobLds*)smem;
   int32_t cnt[kMaxW / kGlobThreads];
-  const uint32_t smax = final_counts<kGlobThreads, kMaxW>(a, a.req[blockIdx.x], cnt);
-  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G, X>(a, blockIdx.x, L, cnt, smax);
+  const ReqDesc rd = a.req[blockIdx.x];
+  const FinalIn in = final_counts<kGlobThreads, kMaxW>(a, blockIdx.x, rd, cnt);
+  final_select<kGlobThreads, kHistBins, kMaxW, kGlobWinCap, kBinCap, 1, G, X>(a, blockIdx.x, rd, L, cnt, in);
   if (threadIdx.x == 0) a.bound[blockIdx.x] = 0u;
 }
 
@@ -1730,7 +1736,7 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
   const ReqDesc rd = a.req[r];
   constexpr int BPT = kFusedMaxW / kFinThreads;
   int32_t cnt[BPT];
-  uint32_t smax = final_counts<kFinThreads, kFusedMaxW>(a, rd, cnt);
+  FinalIn in = final_counts<kFinThreads, kFusedMaxW>(a, r, rd, cnt);
   // beams whose rows overflowed top_k (negative counts): their survivors first (listed in
   // L.pre meanwhile); the counts are read again after them
   if (threadIdx.x == 0) n_over = 0;
@@ -1748,9 +1754,9 @@ __global__ __launch_bounds__(kFinThreads) void select_final_kernel(SelArgs a) {
     }
     wait_stores();
     __syncthreads();
-    smax = final_counts<kFinThreads, kFusedMaxW>(a, rd, cnt);
+    in = final_counts<kFinThreads, kFusedMaxW>(a, r, rd, cnt);
   }
-  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, L, cnt, smax);
+  final_select<kFinThreads, kFusedBins, kFusedMaxW, kFusedWinCap, kFusedBinCap, kFusedWinCap, G, X>(a, r, rd, L, cnt, in);
   __syncthreads();
   if (threadIdx.x == 0) a.bound[r] = 0u;
   if (threadIdx.x < kSyncCopies) a.sync[((size_t)r * kSyncCopies + threadIdx.x) * kSyncStride] = 0ull;
