@@ -677,6 +677,83 @@ struct PilotLds {
   int last;
 };
 
+// One contribution per group of pd.w threads of pilot pd (at most top_k per beam) goes to
+// the pilot buffer; the pilot then counts itself in.  Returns true (in every thread) in the
+// request's last pilot to count in.  Reached by every thread of the workgroup.
+template <bool G, bool WIDE>
+__device__ __forceinline__ bool pilot_contribute(const SelArgs& a, const int4 pd, const ReqDesc& rd, uint64_t best,
+                                                 PilotLds& S) {
+  uint64_t* red64 = S.red64;
+  int& last_s = S.last;
+  const int tid = threadIdx.x;
+  const int r = pd.y, gsz = pd.w;
+  // one contribution per group of gsz threads (at most top_k per beam)
+  const int gl = gsz < 64 ? gsz : 64;
+  if (gl > 1) best = max(best, lane_xor<1>(best));
+  if (gl > 2) best = max(best, lane_xor<2>(best));
+  if (gl > 4) best = max(best, lane_xor<4>(best));
+  if (gl > 8) best = max(best, lane_xor<8>(best));
+  if (gl > 16) best = max(best, lane_xor<16>(best));
+  if (gl > 32) best = max(best, lane_xor<32>(best));
+  if (gsz > 64) {
+    if ((tid & 63) == 0) red64[tid >> 6] = best;
+    __syncthreads();
+    const int w0 = (tid >> 6) & ~((gsz >> 6) - 1);
+    best = red64[w0];
+    for (int w = 1; w < (gsz >> 6); ++w) best = max(best, red64[w0 + w]);
+  }
+  if (tid % gsz == 0) st_dev(&a.pilot_buf[pd.z + tid / gsz], best);
+  wait_stores();
+  __syncthreads();
+  const int n_pilot = WIDE ? (G ? rd.n_pilot_ws : rd.n_pilot_w) : (G ? rd.n_pilot_s : rd.n_pilot);
+  if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(n_pilot - 1);
+  __syncthreads();
+  return last_s;
+}
+
+// The request's last pilot: the W_r-th best key of all contributions bounds the request's
+// W_r-th best pool entry.  PUBLISH: stored with a device-coherent store, then set in every
+// copy of the request's step word.
+template <bool G, bool PUBLISH, bool WIDE>
+__device__ __forceinline__ void pilot_bound(const SelArgs& a, int r, int gsz, const ReqDesc& rd, PilotLds& S) {
+  uint32_t* hist = S.hist;
+  uint32_t* scr = S.scr;
+  uint32_t* red32 = S.red32;
+  int* red = S.red;
+  const int tid = threadIdx.x;
+  const int n_pilot = WIDE ? (G ? rd.n_pilot_ws : rd.n_pilot_w) : (G ? rd.n_pilot_s : rd.n_pilot);
+  constexpr int NP = (WIDE ? kPilotCapWide : kPilotCap) / 256;
+  const int n_ent = n_pilot * (256 / gsz);
+  const uint64_t* pb = a.pilot_buf + rd.pilot_off;
+  uint32_t pk[NP];
+  int nv = 0;
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int q = tid + 256 * k;
+    pk[k] = q < n_ent ? (uint32_t)(ld_dev(&pb[q]) >> 32) : 0u;
+    nv += pk[k] != 0u;
+  }
+  nv = block_sum256(nv, red);
+  uint32_t lo = 0;
+  if (nv >= rd.W)
+    lo = regs_select32<256, NP>([&](int k) { return pk[k]; }, (uint32_t)rd.W, (uint32_t)nv, hist, scr, red32).v;
+  if constexpr (PUBLISH) {
+    // the bound in every copy of the step word, after the bound itself is stored for the
+    // W-of-pool stage (beam workgroups raise it only after they have read the word)
+    if (tid == 0) {
+      st_dev(&a.bound[r], lo);
+      st_dev(&a.pilot_count[r], 0u);
+      wait_stores();
+    }
+    __syncthreads();
+    if (tid < kSyncCopies)
+      st_dev(&a.sync[((size_t)r * kSyncCopies + tid) * kSyncStride], kSyncBound | lo);
+  } else if (tid == 0) {
+    a.bound[r] = lo;
+    a.pilot_count[r] = 0u;
+  }
+}
+
 // Pilot workgroup `pi`.  PUBLISH (pilots inside the per-beam kernel): the request's last
 // pilot stores the bound with a device-coherent store and, once that store is acknowledged,
 // sets the request's ready word that the kernel's beam workgroups wait on.
@@ -684,14 +761,8 @@ struct PilotLds {
 // general kernels' pilot set (up to kPilotCapWide contributions per request).
 template <bool G, bool X, bool PUBLISH, int LT = -1, bool WIDE = false>
 __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S) {
-  uint64_t* red64 = S.red64;
   float* redf = S.redf;
   double* redd = S.redd;
-  uint32_t* hist = S.hist;
-  uint32_t* scr = S.scr;
-  uint32_t* red32 = S.red32;
-  int* red = S.red;
-  int& last_s = S.last;
   const int tid = threadIdx.x;
   const int4 pd = ((const int4*)a.pilot_desc)[pi];
   const int slot = pd.x, r = pd.y, gsz = pd.w;
@@ -756,59 +827,7 @@ __device__ __forceinline__ void pilot_run(const SelArgs& a, int pi, PilotLds& S)
       }
     }
   }
-  // one contribution per group of gsz threads (at most top_k per beam)
-  const int gl = gsz < 64 ? gsz : 64;
-  if (gl > 1) best = max(best, lane_xor<1>(best));
-  if (gl > 2) best = max(best, lane_xor<2>(best));
-  if (gl > 4) best = max(best, lane_xor<4>(best));
-  if (gl > 8) best = max(best, lane_xor<8>(best));
-  if (gl > 16) best = max(best, lane_xor<16>(best));
-  if (gl > 32) best = max(best, lane_xor<32>(best));
-  if (gsz > 64) {
-    if ((tid & 63) == 0) red64[tid >> 6] = best;
-    __syncthreads();
-    const int w0 = (tid >> 6) & ~((gsz >> 6) - 1);
-    best = red64[w0];
-    for (int w = 1; w < (gsz >> 6); ++w) best = max(best, red64[w0 + w]);
-  }
-  if (tid % gsz == 0) st_dev(&a.pilot_buf[pd.z + tid / gsz], best);
-  wait_stores();
-  __syncthreads();
-  const int n_pilot = WIDE ? (G ? rd.n_pilot_ws : rd.n_pilot_w) : (G ? rd.n_pilot_s : rd.n_pilot);
-  if (tid == 0) last_s = atomicAdd(&a.pilot_count[r], 1u) == (uint32_t)(n_pilot - 1);
-  __syncthreads();
-  if (!last_s) return;
-  // the W_r-th best key of all contributions bounds the request's W_r-th best pool entry
-  constexpr int NP = (WIDE ? kPilotCapWide : kPilotCap) / 256;
-  const int n_ent = n_pilot * (256 / gsz);
-  const uint64_t* pb = a.pilot_buf + rd.pilot_off;
-  uint32_t pk[NP];
-  int nv = 0;
-#pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int q = tid + 256 * k;
-    pk[k] = q < n_ent ? (uint32_t)(ld_dev(&pb[q]) >> 32) : 0u;
-    nv += pk[k] != 0u;
-  }
-  nv = block_sum256(nv, red);
-  uint32_t lo = 0;
-  if (nv >= rd.W)
-    lo = regs_select32<256, NP>([&](int k) { return pk[k]; }, (uint32_t)rd.W, (uint32_t)nv, hist, scr, red32).v;
-  if constexpr (PUBLISH) {
-    // the bound in every copy of the step word, after the bound itself is stored for the
-    // W-of-pool stage (beam workgroups raise it only after they have read the word)
-    if (tid == 0) {
-      st_dev(&a.bound[r], lo);
-      st_dev(&a.pilot_count[r], 0u);
-      wait_stores();
-    }
-    __syncthreads();
-    if (tid < kSyncCopies)
-      st_dev(&a.sync[((size_t)r * kSyncCopies + tid) * kSyncStride], kSyncBound | lo);
-  } else if (tid == 0) {
-    a.bound[r] = lo;
-    a.pilot_count[r] = 0u;
-  }
+  if (pilot_contribute<G, WIDE>(a, pd, rd, best, S)) pilot_bound<G, PUBLISH, WIDE>(a, r, gsz, rd, S);
 }
 
 // The general kernels' pilots (the register-resident path runs its pilots inside
