@@ -247,5 +247,15 @@ def grw_backtrack(ws: Workspace, tokens, parents, S: int, sid_out, stream=None):
         _ptr(sid_out, _I32, "sid_out"), _stream(stream)))
 
 
+def selftest_lanes(device=None, stream=None) -> int:
+    """(check, thread) pairs where the device's wave primitives disagree with the shuffle
+    forms they replace; 0 = pass (see include/grw.h).  Synchronises the stream."""
+    buf = torch.empty(_lib.SELFTEST_WORDS, dtype=torch.int32,
+                      device=device if device is not None else torch.device("cuda", torch.cuda.current_device()))
+    v = ctypes.c_int32()
+    _lib.check("grw_selftest_lanes", _L.grw_selftest_lanes(buf.data_ptr(), _stream(stream), ctypes.byref(v)))
+    return v.value
+
+
 from .layout import pack_shared_kv, stored_tensor  # noqa: E402,F401
 from .loop import DecodeLoop  # noqa: E402,F401

@@ -18,13 +18,14 @@ FLAG_NAN_LOGPROB, FLAG_POS_LOGPROB, FLAG_BAD_NODE, FLAG_BAD_PARENT, FLAG_CHILD_M
 FLAG_POOL_CORRUPT = 32
 FLAG_BAD_NOISE = 64
 STAGE_SHARED, STAGE_UNSHARED, STAGE_MERGE = 1, 2, 4
+SELFTEST_WORDS = 3584
 
 EXPORTED = ["grw_ws_create", "grw_ws_destroy", "grw_ws_bind_batch", "grw_beams_init",
             "beam_attn_decode", "beam_attn_decode_stages", "beam_attn_decode_overlap", "beam_select", "beam_select_gumbel",
             "beam_select_logits", "beam_select_ex", "grw_trie_dense_build", "grw_plan_batches", "grw_backtrack",
             "grw_ws_error",
             "grw_ws_splits", "grw_ws_pool_size", "grw_ws_set_wait_limit", "grw_status_str",
-            "beam_select_noalloc"]
+            "beam_select_noalloc", "grw_selftest_lanes"]
 
 
 class GrwLimits(ctypes.Structure):
@@ -85,6 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "grw_ws_pool_size": [vp, i32, vp, ctypes.POINTER(ctypes.c_int64)],
         "grw_ws_set_wait_limit": [vp, i32],
         "beam_select_noalloc": [fp, fp, i32p, i32p, i32p, i32, i32, i32, i32, i32p, i32p, fp, i32p, i32p, vp],
+        "grw_selftest_lanes": [vp, vp, ctypes.POINTER(i32)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)

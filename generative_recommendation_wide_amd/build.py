@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgrw.so")
-SOURCES = ["api.hip", "attn_shared.hip", "attn_unshared.hip", "select.hip"]
+SOURCES = ["api.hip", "attn_shared.hip", "attn_unshared.hip", "select.hip", "selftest.hip"]
 CEILING_LIB = os.path.join(HERE, "libgrw_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 ARCH = "gfx950"

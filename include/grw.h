@@ -437,6 +437,17 @@ int beam_select_noalloc(const float* logprobs, const float* beam_scores, const i
                         int32_t W, int32_t K, int32_t C, int32_t* out_token, int32_t* out_parent,
                         float* out_score, int32_t* out_node, int32_t* device_flags, void* stream);
 
+/* Self-check of the device's wave primitives: the register lane exchanges (DPP quad, row and
+   wave controls, v_permlane16/32_swap), wave scans and reductions that the selection and
+   attention kernels use, each compared bit for bit with the general shuffle it replaces, on
+   one workgroup of 256 threads.  Allocates nothing: `scratch` is a device buffer of at least
+   GRW_SELFTEST_WORDS int32 words owned by the caller (overwritten).  Enqueues on `stream`,
+   synchronises it, and writes the number of (check, thread) pairs that disagree to
+   *mismatches (host pointer): 0 on a correct build and device.  NULL scratch or mismatches:
+   GRW_EINVAL with nothing enqueued.  Diagnostics only. */
+#define GRW_SELFTEST_WORDS 3584
+int grw_selftest_lanes(int32_t* scratch, void* stream, int32_t* mismatches);
+
 const char* grw_status_str(int status);
 
 #ifdef __cplusplus

@@ -84,6 +84,8 @@ def test_null_handles_rejected(clib):
     assert f(None, None, None, 0.0, None, None, None, None, 0, 1, 1, 1, None, None, None, None, None) == 1
     assert clib.grw_backtrack(None, None, None, 1, None, None) == 1
     assert clib.grw_ws_pool_size(None, 0, None, None) == 1
+    clib.grw_selftest_lanes.argtypes = [ctypes.c_void_p] * 3
+    assert clib.grw_selftest_lanes(None, None, None) == 1
 
 
 def test_ceiling_probe_library_is_separate(clib):
