@@ -440,8 +440,8 @@ int beam_select_noalloc(const float* logprobs, const float* beam_scores, const i
 /* Self-check of the device's wave primitives: the register lane exchanges (DPP quad, row and
    wave controls, v_permlane16/32_swap), wave scans and reductions that the selection and
    attention kernels use, each compared bit for bit with the general shuffle it replaces, on
-   one workgroup of 256 threads.  Allocates nothing: `scratch` is a device buffer of at least
-   GRW_SELFTEST_WORDS int32 words owned by the caller (overwritten).  Enqueues on `stream`,
+   one workgroup of 256 threads.  `scratch` is a device buffer of at least GRW_SELFTEST_WORDS
+   int32 words owned by the caller (overwritten).  Enqueues on `stream`,
    synchronises it, and writes the number of (check, thread) pairs that disagree to
    *mismatches (host pointer): 0 on a correct build and device.  NULL scratch or mismatches:
    GRW_EINVAL with nothing enqueued.  Diagnostics only. */
